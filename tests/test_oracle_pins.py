@@ -1,0 +1,649 @@
+"""Pins of the CPU oracle to facts outside itself (CPU only).
+
+Each test checks the oracle against something it does not compute the same
+way: values worked by hand from the pages' definitions (tests/golden), closed
+forms, invariants stated by the pages, exact rational arithmetic, a library
+routine (torch / numpy / scipy), a different algorithm for the same result,
+or brute force on tiny inputs.
+"""
+import itertools
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---------------------------------------------------------------------------
+# Independent helpers
+# ---------------------------------------------------------------------------
+
+def bf16_bits_to_f64(b):
+    b = np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16
+    return b.view(np.float32).astype(np.float64)
+
+
+def exact_bf16(fr: Fraction) -> int:
+    """Correct rounding of an exact rational to bf16 bits, by enumeration of
+    the two neighbouring bf16 values (nearest, ties to the even significand)."""
+    if fr == 0:
+        return 0
+    sign = 0x8000 if fr < 0 else 0
+    a = abs(fr)
+    # Largest power of two <= a.
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= a:
+        e += 1
+    q = Fraction(2) ** (max(e, -126) - 7)          # spacing of bf16 values near a
+    lo = (a // q) * q
+    hi = lo + q
+    if a - lo < hi - a:
+        v = lo
+    elif a - lo > hi - a:
+        v = hi
+    else:
+        v = lo if (a // q) % 2 == 0 else hi
+    if v >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    f = np.float32(float(v))                        # exact: v has <= 8 bits
+    return sign | int(np.array([f], dtype=np.float32).view(np.uint32)[0] >> 16)
+
+
+def torch_bf16_bits(f32: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(f32, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def union_intervals_plan(T, R, E, S, K):
+    """Replicas as the intervals between consecutive values of the union of the
+    cumulative spill totals and the cumulative deficit totals (a merge, not a
+    two-pointer walk).  Spill amounts follow the lowest-id-first reading."""
+    L, C = E // R, S * K
+    load = [sum(T[r * L:(r + 1) * L]) for r in range(R)]
+    spill = []
+    for r in range(R):
+        x = max(load[r] - C, 0)
+        for e in range(r * L, (r + 1) * L):
+            g = min(T[e], x)
+            x -= g
+            if g:
+                spill.append((e, g))
+    deficit = [(r, C - load[r]) for r in range(R) if load[r] < C]
+    A = list(itertools.accumulate(a for _, a in spill))
+    B = list(itertools.accumulate(b for _, b in deficit))
+    U = sorted(set(A) | set(B))
+    reps, prev = [], 0
+    for u in U:
+        i = next(ii for ii, a in enumerate(A) if a >= u)
+        j = next(jj for jj, b in enumerate(B) if b >= u)
+        a_excl = A[i] - spill[i][1]
+        reps.append((spill[i][0], deficit[j][0], u - prev, prev - a_excl))
+        prev = u
+    return reps
+
+
+def stable_sort_slots(topk, pl, R, E, S, K):
+    """slot_of by a stable argsort of the entries by expert, then a walk of
+    each expert's run: first keep_e rows at home, the rest into its replicas."""
+    L, C = E // R, S * K
+    order = np.argsort(np.asarray(topk), kind="stable")
+    slot_of = np.full(len(topk), -1, dtype=np.int64)
+    counts = np.bincount(np.asarray(topk), minlength=E)
+    start = 0
+    for e in range(E):
+        run = order[start:start + counts[e]]
+        start += counts[e]
+        keep = pl.keep[e]
+        for pos, n in enumerate(run):
+            if pos < keep:
+                slot_of[n] = (e // L) * C + pl.home_row_off[e] + pos
+            else:
+                q = pos - keep
+                for j in range(pl.rep_first[e], pl.rep_first[e] + pl.rep_cnt[e]):
+                    so, cnt = pl.rep_spill_off[j], pl.rep_count[j]
+                    if so <= q < so + cnt:
+                        slot_of[n] = pl.rep_host[j] * C + pl.rep_row_off[j] + q - so
+    return slot_of
+
+
+def brute_min_replicas(T, R, E, C):
+    """Smallest number of (expert, non-home rank) pairs with which every rank
+    can receive exactly C entries (max-flow feasibility, scipy)."""
+    from scipy.sparse import csr_matrix
+    from scipy.sparse.csgraph import maximum_flow
+
+    L = E // R
+    NK = sum(T)
+    pairs = [(e, r) for e in range(E) for r in range(R) if r != e // L]
+    src, sink = 0, 1 + E + R
+    big = NK + 1
+    for size in range(len(pairs) + 1):
+        for sub in itertools.combinations(pairs, size):
+            rows, cols, caps = [], [], []
+            for e in range(E):
+                rows += [src, 1 + e]
+                cols += [1 + e, 1 + E + e // L]
+                caps += [T[e], big]
+            for e, r in sub:
+                rows.append(1 + e)
+                cols.append(1 + E + r)
+                caps.append(big)
+            for r in range(R):
+                rows.append(1 + E + r)
+                cols.append(sink)
+                caps.append(C)
+            g = csr_matrix((np.array(caps, dtype=np.int32), (rows, cols)),
+                           shape=(sink + 1, sink + 1))
+            if maximum_flow(g, src, sink).flow_value == NK:
+                return size
+    raise AssertionError("infeasible")
+
+
+def check_plan_invariants(T, pl, R, E, S, K):
+    L, C = E // R, S * K
+    T = np.asarray(T)
+    n = pl.n_rep
+    exp_, host, cnt = pl.rep_expert[:n], pl.rep_host[:n], pl.rep_count[:n]
+    # every rank receives exactly C rows: kept home rows + hosted replica rows
+    for r in range(R):
+        rows = pl.keep[r * L:(r + 1) * L].sum() + cnt[host == r].sum()
+        assert rows == C
+    # every entry of every expert is placed once
+    for e in range(E):
+        assert 0 <= pl.keep[e] <= T[e]
+        assert pl.keep[e] + cnt[exp_ == e].sum() == T[e]
+    assert (cnt > 0).all()
+    assert (host != exp_ // L).all()          # never a replica on the home rank
+    load = np.array([T[r * L:(r + 1) * L].sum() for r in range(R)])
+    assert (load == pl.load).all()
+    for j in range(n):
+        assert load[exp_[j] // L] > C           # only overfull ranks give up tokens
+        assert load[host[j]] < C                # only underfull ranks host replicas
+    # zero replicas iff already balanced
+    assert (n == 0) == bool((load == C).all())
+    # the two-pointer bound
+    assert n <= max(pl.n_spill + pl.n_deficit - 1, 0)
+    # the lowest-id-first reading: inside an overfull rank, spill is a prefix
+    for r in range(R):
+        sp = pl.spill[r * L:(r + 1) * L]
+        te = T[r * L:(r + 1) * L]
+        assert sp.sum() == max(load[r] - C, 0)
+        partial = False
+        for e in range(L):
+            if partial:
+                assert sp[e] == 0
+            elif sp[e] < te[e]:
+                partial = True
+    # replicas of one expert and of one host are consecutive ids
+    for arr in (exp_, host):
+        seen = set()
+        for j in range(n):
+            if j and arr[j] != arr[j - 1]:
+                assert arr[j] not in seen
+            seen.add(arr[j])
+
+
+def random_tiny(rng):
+    R = int(rng.integers(1, 5))
+    L = int(rng.integers(1, 4))
+    E = R * L
+    K = int(rng.integers(1, E + 1))
+    S = int(rng.integers(0, 6))
+    N = R * S
+    topk = np.empty(N * K, dtype=np.int32)
+    skew = rng.uniform(0, 3)
+    p = (np.arange(E) + 1.0) ** -skew
+    p = p[rng.permutation(E)]
+    for t in range(N):
+        topk[t * K:(t + 1) * K] = rng.choice(E, size=K, replace=False, p=p / p.sum())
+    return R, E, S, K, topk
+
+
+# ---------------------------------------------------------------------------
+# bf16 conversions
+# ---------------------------------------------------------------------------
+
+def test_bf16_from_double_matches_torch_on_fp32_values():
+    rng = np.random.default_rng(1)
+    f = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32),
+        (rng.standard_normal(2000) * 1e-38).astype(np.float32),     # subnormal range
+        (rng.standard_normal(2000) * 1e38).astype(np.float32),      # near overflow
+        np.array([0.0, -0.0, 1.0, -1.0, 3.0e38, 3.4e38, 1e-45], dtype=np.float32),
+    ])
+    # exact bf16 ties: 8 significant bits plus a trailing half
+    ties = (np.arange(1, 2000, dtype=np.uint32) << 15 | 0x3F800000 | 0x8000).view(np.float32)
+    f = np.concatenate([f, ties, -ties])
+    ref = torch_bf16_bits(f)
+    got = np.array([oracle.bf16_from_double(float(v)) for v in f], dtype=np.uint16)
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_bf16_from_double_is_correct_rounding_of_doubles():
+    rng = np.random.default_rng(2)
+    vals = list(rng.standard_normal(3000) * 10.0 ** rng.integers(-40, 38, 3000))
+    # doubles just off a bf16 tie (fp32 rounding alone would make them ties)
+    base = 1.0 + 2.0 ** -8
+    vals += [base + 2.0 ** -40, base - 2.0 ** -40, -(base + 2.0 ** -40), base]
+    for v in vals:
+        assert oracle.bf16_from_double(v) == exact_bf16(Fraction(v)), v
+
+
+def test_bf16_to_double_is_the_upper_half_of_fp32():
+    b = np.arange(0, 65536, 97, dtype=np.uint16)
+    b = b[(b & 0x7F80) != 0x7F80]     # finite values
+    ref = bf16_bits_to_f64(b)
+    got = np.array([oracle.bf16_to_double(int(x)) for x in b])
+    np.testing.assert_array_equal(got, ref)
+
+
+# ---------------------------------------------------------------------------
+# route statistics and maxvio
+# ---------------------------------------------------------------------------
+
+def load_golden():
+    with open(os.path.join(GOLDEN, "hand_examples.json")) as f:
+        return json.load(f)["examples"]
+
+
+@pytest.mark.parametrize("ex", load_golden(), ids=lambda ex: ex["name"])
+def test_hand_examples(ex):
+    R, E, S, K = ex["R"], ex["E"], ex["S"], ex["K"]
+    topk = np.array(ex["topk"], dtype=np.int32)
+    T, mv = oracle.route_stats(R, E, S, K, topk)
+    assert T.tolist() == ex["T"]
+    assert mv == ex["maxvio"]
+    pl = oracle.plan(R, E, S, K, T)
+    assert pl.n_rep == ex["n_rep"]
+    for j, rep in enumerate(ex["replicas"]):
+        assert pl.rep_expert[j] == rep["expert"]
+        assert pl.rep_host[j] == rep["host"]
+        assert pl.rep_count[j] == rep["count"]
+        assert pl.rep_spill_off[j] == rep["spill_off"]
+        assert pl.rep_row_off[j] == rep["row_off"]
+    assert pl.keep.tolist() == ex["keep"]
+    assert pl.home_row_off.tolist() == ex["home_row_off"]
+    slot_of, src_of_slot = oracle.slots(R, E, S, K, topk, pl)
+    assert slot_of.tolist() == ex["slot_of"]
+    assert (src_of_slot[slot_of] == np.arange(len(topk))).all()
+
+
+def test_counts_match_bincount_and_sum():
+    rng = np.random.default_rng(3)
+    for _ in range(50):
+        R, E, S, K, topk = random_tiny(rng)
+        T, _ = oracle.route_stats(R, E, S, K, topk)
+        np.testing.assert_array_equal(T, np.bincount(topk, minlength=E))
+        assert T.sum() == R * S * K
+
+
+def test_maxvio_balanced_is_zero():
+    # balanced construction: T_e = Tbar for every e
+    for (R, E, S, K) in [(8, 64, 4096, 8), (4, 16, 128, 2), (2, 8, 12, 4)]:
+        topk = synth.balanced_topk(R * S, E, K)
+        T, mv = oracle.route_stats(R, E, S, K, topk)
+        assert (T == R * S * K // E).all()
+        assert mv == 0.0
+
+
+def test_maxvio_adversarial_closed_form():
+    w = synth.WORKLOADS["adversarial"]
+    topk, _ = synth.routing(w, 0)
+    T, mv = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+    assert (T[:w.K] == w.R * w.S).all() and (T[w.K:] == 0).all()
+    assert mv == w.E / w.K - 1 == 15.0
+
+
+def test_maxvio_hottest_expert_relation():
+    # The explainer's maxvio panel: hottest expert = round((1 + maxvio) * Tbar).
+    for level in (0.5, 1.0, 2.0, 4.0):
+        w = synth.sweep_workload(level, seed=0)
+        topk, _ = synth.routing(w, 0)
+        T, mv = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+        tbar = w.S * w.K * w.R / w.E
+        assert round((1 + mv) * tbar) == T.max()
+        assert abs(mv - level) <= 0.02
+
+
+def test_maxvio_edge_cases():
+    T, mv = oracle.route_stats(2, 4, 0, 2, np.zeros(0, dtype=np.int32))
+    assert mv == 0.0 and (T == 0).all()
+    with pytest.raises(oracle.OracleError):
+        oracle.route_stats(2, 4, 1, 1, np.array([0, 4], dtype=np.int32))
+    with pytest.raises(oracle.OracleError):
+        oracle.route_stats(2, 4, 1, 1, np.array([-1, 0], dtype=np.int32))
+    with pytest.raises(oracle.OracleError):
+        oracle.route_stats(3, 4, 1, 1, np.array([0, 0, 0], dtype=np.int32))   # E % R != 0
+
+
+# ---------------------------------------------------------------------------
+# plan
+# ---------------------------------------------------------------------------
+
+def test_plan_invariants_random_tiny():
+    rng = np.random.default_rng(4)
+    for _ in range(2000):
+        R, E, S, K, topk = random_tiny(rng)
+        T, _ = oracle.route_stats(R, E, S, K, topk)
+        pl = oracle.plan(R, E, S, K, T)
+        check_plan_invariants(T, pl, R, E, S, K)
+
+
+def test_plan_equals_union_of_boundaries():
+    rng = np.random.default_rng(5)
+    for _ in range(1000):
+        R, E, S, K, topk = random_tiny(rng)
+        T, _ = oracle.route_stats(R, E, S, K, topk)
+        pl = oracle.plan(R, E, S, K, T)
+        reps = union_intervals_plan(T.tolist(), R, E, S, K)
+        assert pl.n_rep == len(reps)
+        got = list(zip(pl.rep_expert[:pl.n_rep].tolist(), pl.rep_host[:pl.n_rep].tolist(),
+                       pl.rep_count[:pl.n_rep].tolist(), pl.rep_spill_off[:pl.n_rep].tolist()))
+        assert got == reps
+
+
+@pytest.mark.parametrize("name", ["tiny", "sweep", "dsv3"])
+def test_plan_equals_union_of_boundaries_full(name):
+    w = synth.WORKLOADS[name]
+    topk, _ = synth.routing(w, 0)
+    T, _ = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
+    check_plan_invariants(T, pl, w.R, w.E, w.S, w.K)
+    reps = union_intervals_plan(T.tolist(), w.R, w.E, w.S, w.K)
+    got = list(zip(pl.rep_expert[:pl.n_rep].tolist(), pl.rep_host[:pl.n_rep].tolist(),
+                   pl.rep_count[:pl.n_rep].tolist(), pl.rep_spill_off[:pl.n_rep].tolist()))
+    assert got == reps
+
+
+def test_plan_never_below_brute_force_minimum():
+    rng = np.random.default_rng(6)
+    gaps = []
+    cases = 0
+    while cases < 60:
+        R = int(rng.integers(2, 4))
+        L = int(rng.integers(1, 3))
+        E = R * L
+        S = int(rng.integers(1, 5))
+        K = int(rng.integers(1, min(E, 2) + 1))
+        C = S * K
+        if E * (R - 1) > 8:
+            continue
+        N = R * S
+        topk = np.concatenate([rng.choice(E, size=K, replace=False) for _ in range(N)]).astype(np.int32)
+        T, _ = oracle.route_stats(R, E, S, K, topk)
+        pl = oracle.plan(R, E, S, K, T)
+        lo = brute_min_replicas(T.tolist(), R, E, C)
+        assert pl.n_rep >= lo
+        # a lower bound that any plan obeys
+        load = pl.load
+        assert pl.n_rep >= max(int((load > C).sum()), int((load < C).sum())) or pl.n_rep == 0
+        gaps.append(pl.n_rep - lo)
+        cases += 1
+    # the greedy is near the minimum on these inputs
+    assert max(gaps) <= 2
+
+
+def test_plan_adversarial_closed_form():
+    w = synth.WORKLOADS["adversarial"]
+    topk, _ = synth.routing(w, 0)
+    T, _ = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
+    C = w.C
+    assert pl.n_rep == 15
+    for j in range(14):
+        assert pl.rep_expert[j] == j // 2
+        assert pl.rep_host[j] == j + 1
+        assert pl.rep_count[j] == C
+        assert pl.rep_spill_off[j] == (j % 2) * C
+        assert pl.rep_row_off[j] == 0
+    assert (pl.rep_expert[14], pl.rep_host[14], pl.rep_count[14], pl.rep_spill_off[14]) == (7, 15, C, 0)
+    assert pl.keep[:8].tolist() == [0] * 7 + [C]
+    slot_of, _ = oracle.slots(w.R, w.E, w.S, w.K, topk, pl)
+    so = slot_of.reshape(w.R, w.S, w.K)
+    # expert 7 (k = 7): source ranks 0..7 stay home on rank 0, ranks 8..15 go to rank 15
+    assert (so[:8, :, 7] // C == 0).all() and (so[8:, :, 7] // C == 15).all()
+    # expert 0 (k = 0): source ranks 0..7 go to rank 1, 8..15 to rank 2
+    assert (so[:8, :, 0] // C == 1).all() and (so[8:, :, 0] // C == 2).all()
+    assert (np.bincount(slot_of // C, minlength=w.R) == C).all()
+
+
+def test_plan_balanced_has_no_replica():
+    w = synth.sweep_workload(0.0)
+    topk, _ = synth.routing(w, 0)
+    T, _ = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
+    assert pl.n_rep == 0 and (pl.keep == T).all()
+
+
+# ---------------------------------------------------------------------------
+# slot assignment
+# ---------------------------------------------------------------------------
+
+def check_slots(topk, pl, slot_of, src_of_slot, R, E, S, K):
+    L, C = E // R, S * K
+    NK = R * S * K
+    assert np.array_equal(np.sort(slot_of), np.arange(NK))              # bijection
+    assert np.array_equal(src_of_slot[slot_of], np.arange(NK))
+    # segment table: each segment holds only its expert, in increasing entry order
+    for r in range(R):
+        segs = [(e, pl.home_row_off[e], pl.keep[e]) for e in range(r * L, (r + 1) * L)]
+        segs += [(pl.rep_expert[j], pl.rep_row_off[j], pl.rep_count[j])
+                 for j in range(pl.n_rep) if pl.rep_host[j] == r]
+        for e, off, cnt in segs:
+            src = src_of_slot[r * C + off:r * C + off + cnt]
+            assert (topk[src] == e).all()
+            assert (np.diff(src) > 0).all()
+
+
+def test_slots_random_tiny():
+    rng = np.random.default_rng(7)
+    for _ in range(1000):
+        R, E, S, K, topk = random_tiny(rng)
+        T, _ = oracle.route_stats(R, E, S, K, topk)
+        pl = oracle.plan(R, E, S, K, T)
+        slot_of, src_of_slot = oracle.slots(R, E, S, K, topk, pl)
+        check_slots(topk, pl, slot_of, src_of_slot, R, E, S, K)
+        np.testing.assert_array_equal(slot_of, stable_sort_slots(topk, pl, R, E, S, K))
+
+
+@pytest.mark.parametrize("name", ["tiny", "sweep"])
+def test_slots_full(name):
+    w = synth.WORKLOADS[name]
+    topk, _ = synth.routing(w, 0)
+    T, _ = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
+    slot_of, src_of_slot = oracle.slots(w.R, w.E, w.S, w.K, topk, pl)
+    check_slots(topk, pl, slot_of, src_of_slot, w.R, w.E, w.S, w.K)
+    np.testing.assert_array_equal(slot_of, stable_sort_slots(topk, pl, w.R, w.E, w.S, w.K))
+
+
+# ---------------------------------------------------------------------------
+# dispatch, stand-in expert, combine
+# ---------------------------------------------------------------------------
+
+def tiny_forward(seed=0):
+    w = synth.WORKLOADS["tiny"]
+    topk, gates = synth.routing(w, seed)
+    x = synth.activations(w, seed)
+    T, _ = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
+    slot_of, src_of_slot = oracle.slots(w.R, w.E, w.S, w.K, topk, pl)
+    return w, topk, gates, x, pl, slot_of, src_of_slot
+
+
+def test_dispatch_is_a_gather_of_token_rows():
+    w, topk, gates, x, pl, slot_of, src_of_slot = tiny_forward()
+    buf = oracle.dispatch(w.K, w.H, x, slot_of)
+    np.testing.assert_array_equal(buf, x[src_of_slot // w.K])
+    rows = np.array([0, 5, w.NK - 1, w.C, 3 * w.C + 7], dtype=np.int64)
+    np.testing.assert_array_equal(oracle.dispatch_rows(w.K, w.H, x, src_of_slot, rows), buf[rows])
+
+
+def test_expert_stand_in_matches_torch_rounding():
+    w, topk, gates, x, pl, slot_of, src_of_slot = tiny_forward()
+    buf = oracle.dispatch(w.K, w.H, x, slot_of)
+    rexp = oracle.row_expert(topk, src_of_slot)
+    s = synth.expert_scale(w.E)
+    out = oracle.expert(w.H, buf, rexp, s)
+    ref = (torch.from_numpy(bf16_bits_to_f64(buf).astype(np.float32))
+           * torch.from_numpy(s[rexp])[:, None]).to(torch.bfloat16)
+    np.testing.assert_array_equal(out, ref.view(torch.int16).numpy().view(np.uint16))
+
+
+def test_combine_exact_rational():
+    w, topk, gates, x, pl, slot_of, src_of_slot = tiny_forward()
+    buf = oracle.dispatch(w.K, w.H, x, slot_of)
+    out = oracle.expert(w.H, buf, oracle.row_expert(topk, src_of_slot), synth.expert_scale(w.E))
+    y = oracle.combine(w.K, w.H, out, gates, slot_of)
+    outf = bf16_bits_to_f64(out)
+    rng = np.random.default_rng(8)
+    for t in rng.choice(w.N, size=40, replace=False):
+        for h in rng.choice(w.H, size=8, replace=False):
+            acc = sum(Fraction(float(gates[t * w.K + k])) * Fraction(outf[slot_of[t * w.K + k], h])
+                      for k in range(w.K))
+            assert y[t, h] == exact_bf16(acc)
+
+
+def test_combine_special_cases():
+    w, topk, gates, x, pl, slot_of, src_of_slot = tiny_forward()
+    buf = oracle.dispatch(w.K, w.H, x, slot_of)
+    # one-hot gates pick the k = 0 row exactly
+    onehot = np.zeros_like(gates)
+    onehot[0::w.K] = 1.0
+    np.testing.assert_array_equal(oracle.combine(w.K, w.H, buf, onehot, slot_of),
+                                  buf[slot_of[0::w.K]])
+    # one-hot on the last k
+    onehot = np.zeros_like(gates)
+    onehot[w.K - 1::w.K] = 1.0
+    np.testing.assert_array_equal(oracle.combine(w.K, w.H, buf, onehot, slot_of),
+                                  buf[slot_of[w.K - 1::w.K]])
+    # unit gates on unscaled rows: y = K * x, exact for K a power of two
+    ones = np.ones_like(gates)
+    y = oracle.combine(w.K, w.H, buf, ones, slot_of)
+    ref = torch_bf16_bits(bf16_bits_to_f64(x).astype(np.float32) * w.K)
+    np.testing.assert_array_equal(y, ref)
+    # scaling every gate by 2 doubles y exactly
+    y1 = oracle.combine(w.K, w.H, buf, gates, slot_of)
+    y2 = oracle.combine(w.K, w.H, buf, gates * 2, slot_of)
+    np.testing.assert_array_equal(bf16_bits_to_f64(y2), 2 * bf16_bits_to_f64(y1))
+
+
+def test_forward_tokens_equals_full_chain():
+    w, topk, gates, x, pl, slot_of, src_of_slot = tiny_forward(seed=3)
+    s = synth.expert_scale(w.E)
+    buf = oracle.dispatch(w.K, w.H, x, slot_of)
+    out = oracle.expert(w.H, buf, oracle.row_expert(topk, src_of_slot), s)
+    y = oracle.combine(w.K, w.H, out, gates, slot_of)
+    toks = np.array([0, 1, 17, w.N - 1], dtype=np.int64)
+    yt = oracle.forward_tokens(w.K, w.H, x, topk, gates, slot_of, src_of_slot, s, toks)
+    np.testing.assert_array_equal(yt, y[toks])
+
+
+# ---------------------------------------------------------------------------
+# combine backward
+# ---------------------------------------------------------------------------
+
+def test_combine_bwd_exact_rational():
+    w, topk, gates, x, pl, slot_of, src_of_slot = tiny_forward()
+    buf = oracle.dispatch(w.K, w.H, x, slot_of)
+    out = oracle.expert(w.H, buf, oracle.row_expert(topk, src_of_slot), synth.expert_scale(w.E))
+    dy = synth.activations(w, 0, synth.TAG_DY)
+    d_out, d_gates = oracle.combine_bwd(w.K, w.H, dy, out, gates, slot_of)
+    dyf, outf = bf16_bits_to_f64(dy), bf16_bits_to_f64(out)
+    rng = np.random.default_rng(9)
+    for n in rng.choice(w.NK, size=40, replace=False):
+        t, row = n // w.K, slot_of[n]
+        exact = sum(Fraction(dyf[t, h]) * Fraction(outf[row, h]) for h in range(w.H))
+        l1 = sum(abs(dyf[t, h] * outf[row, h]) for h in range(w.H))
+        assert abs(float(d_gates[n]) - float(exact)) <= 2.0 ** -24 * abs(float(exact)) + 1e-15 * l1
+        for h in rng.choice(w.H, size=8, replace=False):
+            assert d_out[row, h] == exact_bf16(Fraction(float(gates[n])) * Fraction(dyf[t, h]))
+
+
+def test_combine_bwd_special_cases():
+    w, topk, gates, x, pl, slot_of, src_of_slot = tiny_forward()
+    out = oracle.dispatch(w.K, w.H, x, slot_of)
+    # unit gates pass dy through, half gates halve it
+    dy = synth.activations(w, 1, synth.TAG_DY)
+    d_out, _ = oracle.combine_bwd(w.K, w.H, dy, out, np.ones_like(gates), slot_of)
+    np.testing.assert_array_equal(d_out, dy[src_of_slot // w.K])
+    d_out, _ = oracle.combine_bwd(w.K, w.H, dy, out, np.full_like(gates, 0.5), slot_of)
+    np.testing.assert_array_equal(bf16_bits_to_f64(d_out), 0.5 * bf16_bits_to_f64(dy[src_of_slot // w.K]))
+    # one-hot dy at (token t, column h) reads out[slot_of[n], h] for that token only
+    onehot = np.zeros_like(dy)
+    t, h = 37, 11
+    onehot[t, h] = 0x3F80   # 1.0
+    _, d_gates = oracle.combine_bwd(w.K, w.H, onehot, out, gates, slot_of)
+    outf = bf16_bits_to_f64(out)
+    for n in range(w.NK):
+        want = outf[slot_of[n], h] if n // w.K == t else 0.0
+        assert d_gates[n] == np.float32(want)
+
+
+# ---------------------------------------------------------------------------
+# replica-gradient reduction
+# ---------------------------------------------------------------------------
+
+def test_replica_reduce_closed_form_and_zeroing():
+    w = synth.WORKLOADS["adversarial"]
+    topk, _ = synth.routing(w, 0)
+    T, _ = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
+    G = 64
+    cap = w.E + w.R
+    home = np.zeros((w.E, G), dtype=np.float32)
+    rep = np.full((cap, G), 0.375, dtype=np.float32)
+    h2, r2 = oracle.replica_grad_reduce(w.E, pl, G, home, rep)
+    # experts 0..6 have two replicas, expert 7 one, others none
+    assert (h2[:7] == 0.75).all() and (h2[7] == 0.375).all() and (h2[8:] == 0).all()
+    assert (r2[:pl.n_rep] == 0).all() and (r2[pl.n_rep:] == 0.375).all()
+
+
+def test_replica_reduce_identifies_replica_sets():
+    # distinct powers of two per replica make every sum exact and name its terms
+    rng = np.random.default_rng(10)
+    for _ in range(200):
+        R, E, S, K, topk = random_tiny(rng)
+        T, _ = oracle.route_stats(R, E, S, K, topk)
+        pl = oracle.plan(R, E, S, K, T)
+        cap = E + R
+        G = 3
+        rep = np.array([[2.0 ** j] * G for j in range(cap)], dtype=np.float32)
+        home = np.arange(E * G, dtype=np.float32).reshape(E, G) * 2.0 ** 30
+        h2, r2 = oracle.replica_grad_reduce(E, pl, G, home, rep)
+        for e in range(E):
+            js = [j for j in range(pl.n_rep) if pl.rep_expert[j] == e]
+            want = home[e].astype(np.float64) + sum(2.0 ** j for j in js)
+            np.testing.assert_array_equal(h2[e], want.astype(np.float32))
+        assert (r2[:pl.n_rep] == 0).all()
+        np.testing.assert_array_equal(r2[pl.n_rep:], rep[pl.n_rep:])
+
+
+def test_replica_reduce_random_exact_and_at():
+    w, topk, gates, x, pl, slot_of, src_of_slot = tiny_forward()
+    G = w.G
+    cap = w.E + w.R
+    home = synth.normal_f32(0, synth.TAG_GRAD_HOME, w.E * G, 0.01).reshape(w.E, G)
+    rep = synth.normal_f32(0, synth.TAG_GRAD_REP, cap * G, 0.01).reshape(cap, G)
+    h2, r2 = oracle.replica_grad_reduce(w.E, pl, G, home, rep)
+    for e in range(w.E):
+        js = list(range(pl.rep_first[e], pl.rep_first[e] + pl.rep_cnt[e]))
+        if not js:
+            np.testing.assert_array_equal(h2[e], home[e])
+            continue
+        for i in range(0, G, 97):
+            exact = Fraction(float(home[e, i])) + sum(Fraction(float(rep[j, i])) for j in js)
+            l1 = abs(float(home[e, i])) + sum(abs(float(rep[j, i])) for j in js)
+            assert abs(float(h2[e, i]) - float(exact)) <= 2.0 ** -24 * abs(float(exact)) + 1e-15 * l1
+    idx = np.array([0, 5, G - 1])
+    at = oracle.replica_grad_reduce_at(w.E, pl, G, home[:, idx].copy(), rep[:pl.n_rep][:, idx].copy())
+    np.testing.assert_array_equal(at, h2[:, idx])
