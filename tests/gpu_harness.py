@@ -1,0 +1,77 @@
+"""Helpers for the GPU parity tests: upload synthetic inputs, run the path
+through the C-ABI binding, build the stand-in expert, compare with the oracle.
+
+The stand-in expert (not part of the path) multiplies the rows of expert e by
+fp32(1 + e/E) and rounds to bf16; here it runs as plain torch ops on the GPU,
+in the oracle as plain C.
+"""
+import numpy as np
+import torch
+
+import load_balancing_amd as mx
+import oracle
+import synth
+
+
+def shape_of(w) -> mx.Shape:
+    return mx.Shape(w.R, w.E, w.S, w.K, w.H)
+
+
+def to_dev(a: np.ndarray, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.to("cuda", non_blocking=False)
+
+
+def bf16_dev(a_u16: np.ndarray):
+    return to_dev(a_u16.view(np.int16), torch.int16).view(torch.bfloat16)
+
+
+def bits(t) -> np.ndarray:
+    """bf16 tensor -> uint16 bit patterns on the host."""
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def ordinal(b: np.ndarray) -> np.ndarray:
+    """bf16 bits -> integers ordered like the values (+0 and -0 coincide)."""
+    b = b.astype(np.int32)
+    mag = b & 0x7FFF
+    return np.where(b & 0x8000, -mag, mag)
+
+
+def ulp_diff(a: np.ndarray, b: np.ndarray) -> np.ndarray:
+    return np.abs(ordinal(a) - ordinal(b))
+
+
+def stand_in_expert(topk_dev, src_of_slot_dev, scale_dev, buf, rows_per_chunk=1 << 16):
+    """out[r] = bf16(fp32(buf[r]) * scale[expert of the entry at row r])."""
+    out = torch.empty_like(buf)
+    n = buf.shape[0]
+    for r0 in range(0, n, rows_per_chunk):
+        r1 = min(n, r0 + rows_per_chunk)
+        e = topk_dev[src_of_slot_dev[r0:r1].long()].long()
+        out[r0:r1] = (buf[r0:r1].float() * scale_dev[e][:, None]).to(torch.bfloat16)
+    return out
+
+
+def oracle_plan(w, topk):
+    T, mv = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
+    slot_of, src_of_slot = oracle.slots(w.R, w.E, w.S, w.K, topk, pl)
+    return T, mv, pl, slot_of, src_of_slot
+
+
+def compare_plan(gpu: dict, pl: oracle.Plan, E: int, R: int):
+    """Every plan field, bit for bit."""
+    assert gpu["n_rep"] == pl.n_rep
+    assert gpu["n_spill"] == pl.n_spill
+    assert gpu["n_deficit"] == pl.n_deficit
+    assert gpu["max_rep_rank"] == pl.max_rep_rank
+    for f in ("rep_expert", "rep_host", "rep_count", "rep_spill_off", "rep_row_off", "spill",
+              "keep", "home_row_off", "rep_first", "rep_cnt", "load", "rank_rep_first",
+              "rank_rep_cnt"):
+        np.testing.assert_array_equal(gpu[f], getattr(pl, f), err_msg=f)
+    spill_experts = np.nonzero(pl.spill)[0]
+    np.testing.assert_array_equal(gpu["exp_rep_list"][:len(spill_experts)], spill_experts)
+    assert (gpu["exp_rep_list"][len(spill_experts):] == 0).all()

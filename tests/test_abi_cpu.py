@@ -1,0 +1,100 @@
+"""The C-ABI library loads, exports what include/moonep.h declares, and
+validates arguments on the host (CPU only: no call here reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import load_balancing_amd as mx
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(mx.LIB_PATH):
+        from load_balancing_amd import build
+        build.build()
+    return mx.lib()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "moonep.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moonep_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_exports_every_declared_function(L):
+    names = header_functions()
+    assert set(names) == set(mx.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_shape_rules(L):
+    ok = mx.Shape(4, 16, 128, 2, 64)
+    assert mx.moonep_check_shape(ok) == 0
+    bad = [mx.Shape(3, 16, 128, 2, 64),     # E % R
+           mx.Shape(4, 16, 128, 17, 64),    # K > E
+           mx.Shape(4, 16, 128, 0, 64),     # K < 1
+           mx.Shape(4, 16, 128, 2, 60),     # H % 8
+           mx.Shape(4, 16, -1, 2, 64),      # S < 0
+           mx.Shape(0, 16, 128, 2, 64),     # R < 1
+           mx.Shape(2, 2048, 128, 2, 64),   # E above the on-chip plan limit
+           mx.Shape(1024, 1024, 1 << 20, 2, 64)]  # R*S*K >= 2^31, R above limit
+    for s in bad:
+        assert mx.moonep_check_shape(s) == -1, s
+        assert mx.moonep_workspace_bytes(s) == 0
+        assert mx.moonep_plan_bytes(s) == 0
+    assert mx.moonep_check_shape(mx.Shape(8, 64, (1 << 31) // 64, 8, 64)) == -1
+    assert mx.moonep_check_shape(mx.Shape(4, 16, 0, 2, 64)) == 0     # empty is valid
+
+
+def test_sizes_depend_on_shape_only(L):
+    s = mx.Shape(32, 256, 4096, 8, 7168)
+    lay = mx.moonep_plan_layout_of(s)
+    assert lay.cap == 256 + 32
+    assert lay.words == 16 + 5 * lay.cap + 6 * 256 + 3 * 32
+    assert mx.moonep_plan_bytes(s) == lay.words * 4
+    offs = sorted(getattr(lay, f) for f, _ in mx.PlanLayout._fields_ if f not in ("words", "cap"))
+    assert offs[0] == 0 and len(set(offs)) == len(offs)
+    ws = mx.moonep_workspace_bytes(s)
+    assert ws % 256 == 0 and ws >= 256 + 256 * 4
+
+
+def test_host_errors_before_any_launch(L):
+    s = mx.Shape(4, 16, 128, 2, 64)
+    vp = ctypes.c_void_p
+    B = ctypes.byref
+    wsb = mx.moonep_workspace_bytes(s)
+    fake = 0x100000  # never dereferenced: every call below fails validation first
+    # null pointers
+    assert L.moonep_route_stats(B(s), None, vp(fake), vp(fake), vp(fake), wsb, None) == -2
+    assert L.moonep_dispatch(B(s), vp(fake), None, vp(fake), None) == -2
+    # misalignment of a bf16 buffer
+    assert L.moonep_dispatch(B(s), vp(fake + 2), vp(fake), vp(fake * 4), None) == -3
+    # short workspace
+    assert L.moonep_route_stats(B(s), vp(fake), vp(fake), vp(fake), vp(fake), wsb - 1, None) == -4
+    assert L.moonep_plan(B(s), vp(fake), vp(fake), vp(fake), 16, vp(fake), vp(fake * 2),
+                         vp(fake * 3), None) == -4
+    # overlapping dispatch source and destination
+    assert L.moonep_dispatch(B(s), vp(fake), vp(fake * 8), vp(fake + 4096), None) == -6
+    # overlapping combine output and input
+    assert L.moonep_combine(B(s), vp(fake), vp(fake * 8), vp(fake * 9), vp(fake + 1024), None) == -6
+    # negative G, overlapping gradient arrays
+    assert L.moonep_replica_grad_reduce(B(s), vp(fake), ctypes.c_int64(-1), vp(fake), vp(fake * 2),
+                                        None) == -7
+    assert L.moonep_replica_grad_reduce(B(s), vp(fake), ctypes.c_int64(64), vp(fake),
+                                        vp(fake + 64), None) == -6
+    # invalid shape is reported first
+    bad = mx.Shape(3, 16, 128, 2, 64)
+    assert L.moonep_dispatch(B(bad), vp(fake), vp(fake), vp(fake * 4), None) == -1
+    assert L.moonep_read_error(None, 256, None, None) == -2
+
+
+def test_binding_raises_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(mx, "LIB_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(mx, "_lib", None)
+    with pytest.raises(RuntimeError, match="no fallback"):
+        mx.moonep_check_shape(mx.Shape(4, 16, 128, 2, 64))

@@ -1,0 +1,191 @@
+"""GPU parity at the full workload sizes, launched as the benchmark launches.
+
+Counts, maxvio, the plan and both slot maps are compared in full (bit-exact).
+Buffers too large for a full host-side oracle are checked on sampled rows and
+tokens that the oracle computes one by one, plus properties that hold at any
+size (every dispatch row is the right token row; replica rows end at zero;
+rows the reduction must not touch are bit-identical).
+"""
+import numpy as np
+import pytest
+import torch
+
+import load_balancing_amd as mx
+import oracle
+import synth
+from gpu_harness import (bf16_dev, bits, compare_plan, oracle_plan, shape_of, stand_in_expert,
+                         to_dev, ulp_diff)
+
+pytestmark = pytest.mark.gpu
+
+
+def plan_parity(w, topk):
+    T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk)
+    s = shape_of(w)
+    b = mx.allocate(s)
+    d_topk = to_dev(topk)
+    mx.plan_step(b, d_topk)
+    torch.cuda.synchronize()
+    assert mx.moonep_read_error(b.workspace) == mx.DEV_OK
+    np.testing.assert_array_equal(b.expert_counts.cpu().numpy(), T)
+    assert b.maxvio.item() == mv
+    compare_plan(b.plan_fields(), pl, w.E, w.R)
+    np.testing.assert_array_equal(b.slot_of.cpu().numpy(), slot_of)
+    np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot)
+    return b, d_topk, pl, slot_of, src_of_slot
+
+
+def check_dispatch_rows(w, b, d_x, x, src_of_slot, rng, nsample=2048):
+    # property over every row, one rank's buffer at a time
+    src_dev = b.src_of_slot
+    for r in range(w.R):
+        rows = slice(r * w.C, (r + 1) * w.C)
+        want = d_x[src_dev[rows].long() // w.K]
+        assert torch.equal(b.buf[rows].view(torch.int16), want.view(torch.int16)), f"rank {r}"
+    # sampled rows against the oracle's own definition
+    rows = np.unique(np.concatenate([rng.integers(0, w.NK, nsample),
+                                     np.arange(0, w.NK, w.C), np.arange(w.C - 1, w.NK, w.C)]))
+    got = bits(b.buf[torch.from_numpy(rows).cuda()])
+    np.testing.assert_array_equal(got, oracle.dispatch_rows(w.K, w.H, x, src_of_slot, rows))
+
+
+def forward_sampled(w, seed, ntok=1024):
+    topk, gates = synth.routing(w, seed)
+    x = synth.activations(w, seed)
+    scale = synth.expert_scale(w.E)
+    b, d_topk, pl, slot_of, src_of_slot = plan_parity(w, topk)
+    s = shape_of(w)
+    d_x = bf16_dev(x)
+    b.buf.view(torch.int16).fill_(-1)
+    mx.moonep_dispatch(s, d_x, b.slot_of, b.buf)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(seed + 100)
+    check_dispatch_rows(w, b, d_x, x, src_of_slot, rng)
+    out = stand_in_expert(d_topk, b.src_of_slot, to_dev(scale), b.buf)
+    y = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
+    mx.moonep_combine(s, out, to_dev(gates), b.slot_of, y)
+    torch.cuda.synchronize()
+    toks = np.unique(np.concatenate([rng.integers(0, w.N, ntok), [0, w.N - 1]]))
+    want = oracle.forward_tokens(w.K, w.H, x, topk, gates, slot_of, src_of_slot, scale, toks)
+    got = bits(y[torch.from_numpy(toks).cuda()])
+    du = ulp_diff(got, want)
+    assert du.max() <= 1, f"combine off by {du.max()} ulp"
+    return dict(b=b, d_topk=d_topk, pl=pl, slot_of=slot_of, src_of_slot=src_of_slot, x=x,
+                topk=topk, gates=gates, out=out, y=y, scale=scale, exact=float((du == 0).mean()))
+
+
+@pytest.mark.parametrize("level", synth.SWEEP_LEVELS)
+def test_sweep_level_full(level):
+    """The benchmark workload: every output compared in full."""
+    w = synth.sweep_workload(level, seed=0)
+    print(f"[case] {w.name}", flush=True)
+    topk, gates = synth.routing(w, 0)
+    x = synth.activations(w, 0)
+    scale = synth.expert_scale(w.E)
+    b, d_topk, pl, slot_of, src_of_slot = plan_parity(w, topk)
+    if level == 0.0:
+        assert pl.n_rep == 0
+    s = shape_of(w)
+    d_x = bf16_dev(x)
+    b.buf.view(torch.int16).fill_(-1)
+    mx.moonep_dispatch(s, d_x, b.slot_of, b.buf)
+    o_buf = oracle.dispatch(w.K, w.H, x, slot_of)
+    np.testing.assert_array_equal(bits(b.buf), o_buf)
+    out = stand_in_expert(d_topk, b.src_of_slot, to_dev(scale), b.buf)
+    o_out = oracle.expert(w.H, o_buf, oracle.row_expert(topk, src_of_slot), scale)
+    del o_buf
+    np.testing.assert_array_equal(bits(out), o_out)
+    y = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
+    mx.moonep_combine(s, out, to_dev(gates), b.slot_of, y)
+    o_y = oracle.combine(w.K, w.H, o_out, gates, slot_of)
+    du = ulp_diff(bits(y), o_y)
+    assert du.max() <= 1
+    print(f"[sweep {level}] n_rep={pl.n_rep} combine exact fraction={float((du == 0).mean()):.6f}")
+
+
+def test_dsv3_forward_sampled():
+    w = synth.WORKLOADS["dsv3"]
+    print(f"[case] {w.name}", flush=True)
+    r = forward_sampled(w, 0)
+    assert r["pl"].n_rep > 0
+
+
+def test_adversarial_forward_sampled():
+    w = synth.WORKLOADS["adversarial"]
+    print(f"[case] {w.name}", flush=True)
+    r = forward_sampled(w, 0)
+    assert r["pl"].n_rep == 15
+    # uniform gates 1/8 over 8 rows: y = bf16(sum of the 8 scaled copies / 8)
+    assert r["exact"] > 0.99
+
+
+def test_dsv3_backward_sampled():
+    """Combine backward and the replica-gradient reduction at the
+    DeepSeek-V3-like shape with 7168 x 2048 expert weight-gradients."""
+    w = synth.WORKLOADS["dsv3_bwd"]
+    print(f"[case] {w.name}", flush=True)
+    seed = 0
+    topk, gates = synth.routing(w, seed)
+    x = synth.activations(w, seed)
+    scale = synth.expert_scale(w.E)
+    b, d_topk, pl, slot_of, src_of_slot = plan_parity(w, topk)
+    s = shape_of(w)
+    mx.moonep_dispatch(s, bf16_dev(x), b.slot_of, b.buf)
+    out = stand_in_expert(d_topk, b.src_of_slot, to_dev(scale), b.buf)
+    del b.buf
+    dy = synth.activations(w, seed, synth.TAG_DY)
+    d_dy = bf16_dev(dy)
+    d_gates = to_dev(gates)
+    d_out = torch.empty_like(out)
+    d_out.view(torch.int16).fill_(-1)
+    d_g = torch.full((w.NK,), float("nan"), dtype=torch.float32, device="cuda")
+    mx.moonep_combine_bwd(s, d_dy, out, d_gates, b.slot_of, d_out, d_g)
+    torch.cuda.synchronize()
+
+    # every d_out row is gate * dy of its token (property at full size, exact
+    # when the gate is a power of two, so check against the oracle on samples)
+    assert not (d_out.view(torch.int16) == -1).all(1).any()
+    rng = np.random.default_rng(7)
+    ents = np.unique(np.concatenate([rng.integers(0, w.NK, 1024), [0, w.NK - 1]]))
+    toks = np.unique(ents // w.K)
+    # oracle sub-problem: those tokens, all their K entries
+    sub_ent = (toks[:, None] * w.K + np.arange(w.K)).ravel()
+    rows = slot_of[sub_ent].astype(np.int64)
+    buf_rows = oracle.dispatch_rows(w.K, w.H, x, src_of_slot, rows)
+    out_rows = oracle.expert(w.H, buf_rows, topk[src_of_slot[rows]], scale)
+    o_dout, o_dg = oracle.combine_bwd(w.K, w.H, dy[toks], out_rows, gates[sub_ent],
+                                      np.arange(len(sub_ent), dtype=np.int32))
+    np.testing.assert_array_equal(bits(d_out[torch.from_numpy(rows).cuda()]), o_dout)
+    g = d_g[torch.from_numpy(sub_ent).cuda()].cpu().numpy().astype(np.float64)
+    f = lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    l1 = np.abs(f(dy[toks]).repeat(w.K, 0) * f(out_rows)).sum(1)
+    assert (np.abs(g - o_dg) <= 1e-5 * l1).all()
+    del out, d_out, d_dy
+
+    # replica-gradient reduction, G = 7168 * 2048
+    G = w.G
+    cap = w.E + w.R
+    n = pl.n_rep
+    home = torch.empty((w.E, G), dtype=torch.float32, device="cuda")
+    rep = torch.empty((cap, G), dtype=torch.float32, device="cuda")
+    hbuf = np.empty(G, dtype=np.float32)
+    for e in range(w.E):
+        home[e] = torch.from_numpy(synth.normal_f32_into(hbuf, seed, synth.TAG_GRAD_HOME, 0.01,
+                                                         start=e * G)).cuda()
+    for j in range(n):
+        rep[j] = torch.from_numpy(synth.normal_f32_into(hbuf, seed, synth.TAG_GRAD_REP, 0.01,
+                                                        start=j * G)).cuda()
+    rep[n:].view(torch.int32).fill_(0x7FC01234)                # sentinel: must stay
+    idx = np.unique(np.concatenate([rng.integers(0, G, 4096), [0, G - 1]]))
+    d_idx = torch.from_numpy(idx).cuda()
+    home_at = home[:, d_idx].cpu().numpy()
+    rep_at = rep[:n][:, d_idx].cpu().numpy()
+    untouched = torch.from_numpy(np.nonzero(pl.rep_cnt == 0)[0]).cuda()
+    home_keep = home[untouched].clone()
+    mx.moonep_replica_grad_reduce(s, b.plan, G, home, rep)
+    torch.cuda.synchronize()
+    want = oracle.replica_grad_reduce_at(w.E, pl, G, home_at, rep_at)
+    np.testing.assert_array_equal(home[:, d_idx].cpu().numpy(), want)
+    assert torch.equal(home[untouched], home_keep)
+    assert bool((rep[:n].view(torch.int32) == 0).all())
+    assert bool((rep[n:].view(torch.int32) == 0x7FC01234).all())

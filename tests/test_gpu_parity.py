@@ -1,0 +1,199 @@
+"""GPU parity at sizes the oracle covers element by element.
+
+Every case runs the whole path through the C-ABI (route_stats, plan,
+dispatch, stand-in expert, combine, combine_bwd, replica_grad_reduce) and
+compares every output with the CPU oracle:
+  counts, maxvio, plan, slot maps, dispatch buffer, d_out, replica grads: bit-exact;
+  combine output: within 1 bf16 ulp (fp32 accumulation against the fp64 oracle);
+  gate gradients: |gpu - oracle| <= 1e-5 * sum_h |dy_h * out_h|.
+"""
+from dataclasses import replace
+
+import numpy as np
+import pytest
+import torch
+
+import load_balancing_amd as mx
+import oracle
+import synth
+from gpu_harness import (bf16_dev, bits, compare_plan, oracle_plan, shape_of, stand_in_expert,
+                         to_dev, ulp_diff)
+
+pytestmark = pytest.mark.gpu
+
+
+def bf16_f64(b):
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def run_and_compare(w, seed, topk=None, gates=None, G=None):
+    print(f"[case] {w} seed={seed}", flush=True)
+    if topk is None:
+        topk, gates = synth.routing(w, seed)
+    x = synth.activations(w, seed)
+    dy = synth.activations(w, seed, synth.TAG_DY)
+    scale = synth.expert_scale(w.E)
+    G = w.G if G is None else G
+    cap = w.E + w.R
+    home = synth.normal_f32(seed, synth.TAG_GRAD_HOME, w.E * G, 0.01).reshape(w.E, G)
+    rep = synth.normal_f32(seed, synth.TAG_GRAD_REP, cap * G, 0.01).reshape(cap, G)
+
+    # ---- oracle ----------------------------------------------------------
+    T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk)
+    o_buf = oracle.dispatch(w.K, w.H, x, slot_of)
+    o_out = oracle.expert(w.H, o_buf, oracle.row_expert(topk, src_of_slot), scale)
+    o_y = oracle.combine(w.K, w.H, o_out, gates, slot_of)
+    o_dout, o_dg = oracle.combine_bwd(w.K, w.H, dy, o_out, gates, slot_of)
+    o_home, o_rep = oracle.replica_grad_reduce(w.E, pl, G, home, rep)
+
+    # ---- GPU through the C-ABI ------------------------------------------
+    s = shape_of(w)
+    b = mx.allocate(s)
+    d_topk = to_dev(topk)
+    d_gates = to_dev(gates)
+    d_x = bf16_dev(x)
+    d_dy = bf16_dev(dy)
+    b.buf.view(torch.int16).fill_(-1)                      # sentinel
+    mx.plan_step(b, d_topk)
+    mx.moonep_dispatch(s, d_x, b.slot_of, b.buf)
+    out = stand_in_expert(d_topk, b.src_of_slot, to_dev(scale), b.buf)
+    y = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
+    mx.moonep_combine(s, out, d_gates, b.slot_of, y)
+    d_out = torch.empty_like(out)
+    d_out.view(torch.int16).fill_(-1)
+    d_g = torch.full((w.NK,), float("nan"), dtype=torch.float32, device="cuda")
+    mx.moonep_combine_bwd(s, d_dy, out, d_gates, b.slot_of, d_out, d_g)
+    d_home = to_dev(home)
+    d_rep = to_dev(rep)
+    mx.moonep_replica_grad_reduce(s, b.plan, G, d_home, d_rep)
+    torch.cuda.synchronize()
+    assert mx.moonep_read_error(b.workspace) == mx.DEV_OK
+
+    # ---- compare -----------------------------------------------------------
+    np.testing.assert_array_equal(b.expert_counts.cpu().numpy(), T)
+    assert b.maxvio.item() == mv
+    compare_plan(b.plan_fields(), pl, w.E, w.R)
+    np.testing.assert_array_equal(b.slot_of.cpu().numpy(), slot_of)
+    np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot)
+    np.testing.assert_array_equal(bits(b.buf), o_buf)
+    np.testing.assert_array_equal(bits(out), o_out)
+    y_b = bits(y)
+    du = ulp_diff(y_b, o_y)
+    assert du.max(initial=0) <= 1, f"combine off by {du.max()} ulp"
+    np.testing.assert_array_equal(bits(d_out), o_dout)
+    g_gpu = d_g.cpu().numpy().astype(np.float64)
+    if w.NK:
+        l1 = np.abs(bf16_f64(dy)[np.arange(w.NK) // w.K] * bf16_f64(o_out)[slot_of]).sum(1)
+        err = np.abs(g_gpu - o_dg.astype(np.float64))
+        assert (err <= 1e-5 * l1 + 1e-30).all(), f"gate grad err {err.max()}"
+    np.testing.assert_array_equal(d_home.cpu().numpy(), o_home)
+    np.testing.assert_array_equal(d_rep.cpu().numpy(), o_rep)
+    return {"exact_y": float((du == 0).mean()) if du.size else 1.0, "n_rep": pl.n_rep}
+
+
+def test_tiny_config_full_chain():
+    w = synth.WORKLOADS["tiny"]
+    r = run_and_compare(w, 0)
+    assert r["n_rep"] > 0
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_tiny_other_seeds(seed):
+    run_and_compare(synth.WORKLOADS["tiny"], seed)
+
+
+EDGE = [
+    # ragged entry count (NK = 222) and 3 vectors per row
+    synth.Workload("ragged", 3, 6, 37, 2, 24, "zipf", alpha=1.5, G=40),
+    # one rank: nothing to balance
+    synth.Workload("one_rank", 1, 4, 50, 3, 16, "zipf", alpha=1.0, G=16),
+    # one expert per rank, every expert chosen by every token
+    synth.Workload("k_eq_e", 4, 4, 33, 4, 8, "zipf", alpha=0.5, G=12),
+    # a row of 65 vectors crosses a wave
+    synth.Workload("wide_row", 5, 20, 300, 3, 520, "zipf", alpha=1.3, G=1000),
+    # all tokens to experts 0..7 of rank 0, uniform gates
+    synth.Workload("adversarial_small", 16, 128, 64, 8, 64, "fixed", gates="uniform", G=64),
+    # heavy skew over many segments
+    synth.Workload("heavy_skew", 8, 64, 700, 8, 136, "zipf", alpha=2.0, G=2048 + 3),
+    # balanced routing: no replica
+    synth.Workload("balanced", 8, 64, 512, 8, 64, "balanced", G=64),
+    # G not a multiple of 4 (scalar reduce path)
+    synth.Workload("odd_G", 4, 16, 128, 2, 64, "zipf", alpha=1.0, G=1001),
+]
+
+
+@pytest.mark.parametrize("w", EDGE, ids=lambda w: w.name)
+def test_edge_shapes(w):
+    run_and_compare(w, 0)
+
+
+def test_empty_input():
+    w = synth.Workload("empty", 2, 8, 0, 2, 64, "zipf", G=16)
+    s = shape_of(w)
+    b = mx.allocate(s)
+    e = torch.empty(0, dtype=torch.int32, device="cuda")
+    b.expert_counts.fill_(-7)
+    b.maxvio.fill_(3.0)
+    mx.plan_step(b, e)
+    x = torch.empty((0, w.H), dtype=torch.bfloat16, device="cuda")
+    mx.moonep_dispatch(s, x, b.slot_of, b.buf)
+    mx.moonep_combine(s, b.buf, torch.empty(0, device="cuda"), b.slot_of, x)
+    torch.cuda.synchronize()
+    assert (b.expert_counts.cpu() == 0).all() and b.maxvio.item() == 0.0
+    f = b.plan_fields()
+    assert f["n_rep"] == 0 and (f["keep"] == 0).all()
+
+
+def test_bad_expert_id_sets_error_word_and_stays_in_bounds():
+    w = synth.WORKLOADS["tiny"]
+    topk, gates = synth.routing(w, 0)
+    topk = topk.copy()
+    topk[5] = w.E + 3
+    topk[77] = -1
+    s = shape_of(w)
+    b = mx.allocate(s)
+    d_topk = to_dev(topk)
+    mx.plan_step(b, d_topk)
+    torch.cuda.synchronize()
+    assert mx.moonep_read_error(b.workspace) == mx.DEV_BAD_EXPERT_ID
+    assert mx.moonep_read_error(b.workspace) == mx.DEV_OK        # read clears it
+    so = b.slot_of.cpu().numpy()
+    assert so[5] == -1 and so[77] == -1
+    # the other entries still form valid distinct slots
+    rest = np.delete(so, [5, 77])
+    assert (rest >= 0).all() and (rest < w.NK).all() and len(set(rest.tolist())) == rest.size
+
+
+def test_repeat_is_bitwise_deterministic():
+    w = replace(synth.WORKLOADS["tiny"], S=1000)
+    topk, gates = synth.routing(w, 4)
+    s = shape_of(w)
+    d_topk, d_gates = to_dev(topk), to_dev(gates)
+    d_x = bf16_dev(synth.activations(w, 4))
+    results = []
+    for _ in range(2):
+        b = mx.allocate(s)
+        mx.plan_step(b, d_topk)
+        mx.moonep_dispatch(s, d_x, b.slot_of, b.buf)
+        y = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
+        mx.moonep_combine(s, b.buf, d_gates, b.slot_of, y)   # expert_out may be buf itself
+        torch.cuda.synchronize()
+        results.append((b.plan.cpu(), b.slot_of.cpu(), b.src_of_slot.cpu(), bits(b.buf), bits(y)))
+    for a, c in zip(*results):
+        assert np.array_equal(np.asarray(a), np.asarray(c))
+
+
+def test_plan_with_several_chunk_batches_per_wave():
+    # 2M entries: each wave walks two batches of 16 chunks
+    w = synth.Workload("long_segments", 16, 64, 16384, 8, 8, "zipf", alpha=1.1)
+    topk, _ = synth.routing(w, 0)
+    T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk)
+    s = shape_of(w)
+    b = mx.allocate(s)
+    mx.plan_step(b, to_dev(topk))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(b.expert_counts.cpu().numpy(), T)
+    assert b.maxvio.item() == mv
+    compare_plan(b.plan_fields(), pl, w.E, w.R)
+    np.testing.assert_array_equal(b.slot_of.cpu().numpy(), slot_of)
+    np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot)
