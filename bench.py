@@ -1,0 +1,272 @@
+"""Benchmark of the balanced expert-parallel hot path on one MI355X.
+
+Workload: the maxvio sweep shape -- R=8 logical ranks, E=64 experts, S=4096
+tokens per rank, K=8, H=2048 -- at maxvio 0, 0.5, 1, 2 and 4 (Zipf routing,
+exponent per level from tests/golden/sweep_alpha.json; level 0 balanced).
+Step i runs the whole path on level i mod 5, with every input resident in HBM:
+route_stats -> plan -> dispatch -> combine (identity expert, reading the
+dispatch buffer in place) -> combine_bwd -> replica_grad_reduce (expert
+weight-gradients of 2048 x 1408 fp32).
+
+Reported value: dispatch+combine GB/s = algorithmic bytes of the two calls
+divided by their HIP-event time inside the timed steps.  Algorithmic bytes
+per call (what the call must move at least):
+  dispatch    = N*H*2 (read x once) + NK*H*2 (write rows) + NK*4 (slot_of)
+  combine     = NK*H*2 (read rows) + N*H*2 (write y) + NK*8 (slot_of, gates)
+  combine_bwd = N*H*2 + 2*NK*H*2 + NK*12
+  reduce      = sum over experts with replicas of (n_e + 2)*4G + n_rep*4G
+Also printed: per-call microseconds, plan latency per maxvio level, the
+roofline of the dominant kernel, and the CPU oracle timed on every level.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+CALLS = ("route_stats", "plan", "dispatch", "combine", "combine_bwd", "replica_grad_reduce")
+KERNEL_OF = {"dispatch": "dispatch_kernel", "combine": "combine_kernel",
+             "combine_bwd": "combine_bwd_kernel", "replica_grad_reduce": "replica_reduce_kernel"}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sweep.json")
+
+
+def algorithmic_bytes(R, S, K, H, G=0, reps=None):
+    N, NK = R * S, R * S * K
+    d = {
+        "dispatch": N * H * 2 + NK * H * 2 + NK * 4,
+        "combine": NK * H * 2 + N * H * 2 + NK * 8,
+        "combine_bwd": N * H * 2 + 2 * NK * H * 2 + NK * 12,
+    }
+    if reps is not None:
+        n_rep = int(sum(reps))
+        d["replica_grad_reduce"] = sum((n + 2) * 4 * G for n in reps if n) + n_rep * 4 * G
+    return d
+
+
+def source_hash():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "load_balancing_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(levels, seed):
+    """The CPU oracle, single-threaded, on the forward of every maxvio level."""
+    import oracle
+    import synth
+
+    t_plan = t_disp = t_comb = 0.0
+    dc = 0
+    for level in levels:
+        wl = synth.sweep_workload(level, seed)
+        topk, gates = synth.routing(wl, seed)
+        x = synth.activations(wl, seed)
+        t0 = time.perf_counter()
+        T, _ = oracle.route_stats(wl.R, wl.E, wl.S, wl.K, topk)
+        pl = oracle.plan(wl.R, wl.E, wl.S, wl.K, T)
+        slot_of, _ = oracle.slots(wl.R, wl.E, wl.S, wl.K, topk, pl)
+        t1 = time.perf_counter()
+        buf = oracle.dispatch(wl.K, wl.H, x, slot_of)
+        t2 = time.perf_counter()
+        oracle.combine(wl.K, wl.H, buf, gates, slot_of)
+        t3 = time.perf_counter()
+        del buf
+        b = algorithmic_bytes(wl.R, wl.S, wl.K, wl.H)
+        dc += b["dispatch"] + b["combine"]
+        t_plan += t1 - t0
+        t_disp += t2 - t1
+        t_comb += t3 - t2
+    return {"value": round(dc / (t_disp + t_comb) / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"one forward step at each maxvio level {list(levels)} (seed {seed}), "
+                      f"single thread: route_stats+plan+slots {1e3 * t_plan:.1f} ms, dispatch "
+                      f"{1e3 * t_disp:.1f} ms, combine {1e3 * t_comb:.1f} ms in total; value = "
+                      f"dispatch+combine algorithmic bytes / their time"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-copy-probe", action="store_true",
+                    help="skip the untimed 1 GiB copy used to calibrate HBM counters")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(json.dumps({"error": "this build measures one GPU: R logical ranks are slices of one "
+                                   "device's HBM, so --gpus must be 1"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import load_balancing_amd as mx
+    import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    base = synth.WORKLOADS["sweep"]
+    R, E, S, K, H, G = base.R, base.E, base.S, base.K, base.H, base.G
+    N, NK = R * S, R * S * K
+    s = mx.Shape(R, E, S, K, H)
+    levels = list(synth.SWEEP_LEVELS)
+
+    # ---- inputs, resident in HBM ------------------------------------------
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    topks, gatess = [], []
+    for lv in levels:
+        wl = synth.sweep_workload(lv, args.seed)
+        t, g = synth.routing(wl, args.seed)
+        topks.append(up(t))
+        gatess.append(up(g))
+    x = up(synth.activations(base, args.seed).view(np.int16)).view(torch.bfloat16)
+    dy = up(synth.activations(base, args.seed, synth.TAG_DY).view(np.int16)).view(torch.bfloat16)
+    cap = E + R
+    home = up(synth.normal_f32(args.seed, synth.TAG_GRAD_HOME, E * G, 0.01))
+    rep = up(synth.normal_f32(args.seed, synth.TAG_GRAD_REP, cap * G, 0.01))
+    b = mx.allocate(s, dev)
+    y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    d_out = torch.empty((NK, H), dtype=torch.bfloat16, device=dev)
+    d_g = torch.empty(NK, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i, ev=None):
+        lv = i % len(levels)
+        tk, gt = topks[lv], gatess[lv]
+        calls = (
+            lambda: mx.moonep_route_stats(s, tk, b.expert_counts, b.maxvio, b.workspace, stream),
+            lambda: mx.moonep_plan(s, tk, b.expert_counts, b.workspace, b.plan, b.slot_of,
+                                   b.src_of_slot, stream),
+            lambda: mx.moonep_dispatch(s, x, b.slot_of, b.buf, stream),
+            lambda: mx.moonep_combine(s, b.buf, gt, b.slot_of, y, stream),
+            lambda: mx.moonep_combine_bwd(s, dy, b.buf, gt, b.slot_of, d_out, d_g, stream),
+            lambda: mx.moonep_replica_grad_reduce(s, b.plan, G, home, rep, stream),
+        )
+        for c, fn in enumerate(calls):
+            if ev is not None:
+                ev[c].record(stream)
+            fn()
+        if ev is not None:
+            ev[len(calls)].record(stream)
+
+    # replica counts per level (for the reduce's algorithmic bytes)
+    reps_per_level = []
+    for lv in range(len(levels)):
+        step(lv)
+        torch.cuda.synchronize()
+        f = b.plan_fields()
+        reps_per_level.append([int(c) for c in f["rep_cnt"]])
+        assert mx.moonep_read_error(b.workspace) == 0
+
+    if not args.no_copy_probe:
+        # untimed plain copy of exactly 1 GiB: the HBM-counter calibration kernel
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(CALLS) + 1)]
+              for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    per_call = {c: [] for c in CALLS}
+    per_level = {lv: {c: [] for c in CALLS} for lv in levels}
+    for i in range(args.steps):
+        lv = levels[i % len(levels)]
+        for c, name in enumerate(CALLS):
+            ms = events[i][c].elapsed_time(events[i][c + 1])
+            per_call[name].append(ms)
+            per_level[lv][name].append(ms)
+    mean = lambda v: sum(v) / len(v)
+    us = {c: round(1e3 * mean(v), 2) for c, v in per_call.items()}
+
+    byt = algorithmic_bytes(R, S, K, H)
+    dc_bytes = byt["dispatch"] + byt["combine"]
+    dc_s = 1e-3 * (mean(per_call["dispatch"]) + mean(per_call["combine"]))
+    value = dc_bytes / dc_s / 1e9
+    plan_us = {f"{lv:g}": round(1e3 * (mean(per_level[lv]["route_stats"]) +
+                                      mean(per_level[lv]["plan"])), 2)
+               for lv in levels if per_level[lv]["plan"]}
+    pv = list(plan_us.values())
+    kern = {}
+    for name in ("dispatch", "combine", "combine_bwd", "replica_grad_reduce"):
+        if name == "replica_grad_reduce":
+            per_lv = []
+            for li, lv in enumerate(levels):
+                if per_level[lv][name]:
+                    bb = algorithmic_bytes(R, S, K, H, G, reps_per_level[li])[name]
+                    per_lv.append(bb / (1e-3 * mean(per_level[lv][name])) / 1e9 if bb else None)
+            vals = [v for v in per_lv if v]
+            gbps = mean(vals) if vals else None
+            nbytes = None
+        else:
+            nbytes = byt[name]
+            gbps = nbytes / (1e-3 * mean(per_call[name])) / 1e9
+        kern[name] = {"us": us[name], "GBps": round(gbps, 1) if gbps else None,
+                      "frac": round(gbps / HBM_PEAK_GBPS, 4) if gbps else None,
+                      "bytes_per_launch": nbytes}
+    dominant = max(("dispatch", "combine", "combine_bwd"), key=lambda k: us[k])
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        if t.get("source_hash") == source_hash() and dominant in t.get("kernels", {}):
+            traffic = t["kernels"][dominant]["hbm_bytes_per_launch"]
+    roof = {"bound": "hbm", "kernel": KERNEL_OF[dominant],
+            "achieved": kern[dominant]["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+            "frac": kern[dominant]["frac"], "traffic": traffic,
+            "algorithmic_bytes_per_launch": byt[dominant]}
+
+    result = {
+        "metric": "dispatch+combine GB/s (% HBM peak) and plan latency µs vs maxvio",
+        "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(1e3 * wall / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "maxvio sweep R8 E64 S4096 K8 H2048, maxvio 0/0.5/1/2/4 "
+                               "cycled per step; backward weight-grads 2048x1408 fp32",
+                   "R": R, "E": E, "S": S, "K": K, "H": H, "G": G,
+                   "global_batch": N, "parallelism": "1 GPU, 8 logical ranks"},
+        "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
+        "value_def": "dispatch+combine algorithmic bytes / their HIP-event time",
+        "forward_GBps_incl_plan": round(dc_bytes / (1e-3 * (mean(per_call["dispatch"]) +
+                                                            mean(per_call["combine"]) +
+                                                            mean(per_call["route_stats"]) +
+                                                            mean(per_call["plan"]))) / 1e9, 1),
+        "tokens_per_s_forward": round(N / (1e-3 * sum(mean(per_call[c]) for c in CALLS[:4])), 0),
+        "plan_us_vs_maxvio": plan_us,
+        "plan_spread": round((max(pv) - min(pv)) / min(pv), 4) if pv else None,
+        "breakdown_us": us,
+        "kernels": kern,
+        "replicas_per_level": {f"{lv:g}": int(sum(r)) for lv, r in zip(levels, reps_per_level)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(levels, args.seed)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
