@@ -104,7 +104,7 @@ def main():
                     help="skip the untimed 1 GiB copy used to calibrate HBM counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print(json.dumps({"error": "this build measures one GPU: R logical ranks are slices of one "
+        print(json.dumps({"error": "this benchmark measures one GPU: R logical ranks are slices of one "
                                    "device's HBM, so --gpus must be 1"}))
         sys.exit(2)
 
@@ -228,12 +228,17 @@ def main():
                       "frac": round(gbps / HBM_PEAK_GBPS, 4) if gbps else None,
                       "bytes_per_launch": nbytes}
     dominant = max(("dispatch", "combine", "combine_bwd"), key=lambda k: us[k])
-    traffic = None
+    # HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary,
+    # only while the kernel sources are those the counters were taken on.
+    measured = {}
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        if t.get("source_hash") == source_hash() and dominant in t.get("kernels", {}):
-            traffic = t["kernels"][dominant]["hbm_bytes_per_launch"]
+        if t.get("source_hash") == source_hash():
+            measured = {k: v["hbm_bytes_per_launch"] for k, v in t.get("kernels", {}).items()}
+    for name in kern:
+        kern[name]["traffic"] = measured.get(name)
+    traffic = measured.get(dominant)
     roof = {"bound": "hbm", "kernel": KERNEL_OF[dominant],
             "achieved": kern[dominant]["GBps"], "peak": HBM_PEAK_GBPS, "unit": "GB/s",
             "frac": kern[dominant]["frac"], "traffic": traffic,

@@ -8,120 +8,175 @@
 // aipricedb.com README excerpt adds that the copy from the communication
 // buffer into a user buffer is what this removes.
 //
-// All three are HBM-bound streams of 16-byte bf16 vectors (8 per lane).  Token
-// rows are read once; each of a token's K rows of the buffer is one contiguous
-// 2H-byte run, so every store and load is fully coalesced.  Write-once
-// streams use non-temporal stores.
+// All three are HBM-bound streams of 16-byte bf16 vectors (8 per lane); each
+// of a token's K rows of the buffer is one contiguous 2H-byte run, so every
+// access is fully coalesced, and token rows are read once.  Combine and its
+// backward give one workgroup to one token: its K destination rows and gates
+// are uniform (scalar) loads and all K row loads of a thread are issued before
+// any use (out-of-range slots read row 0 and are masked afterwards, so no
+// branch splits the loads).  Dispatch paces its stores instead (see there).
+// Write-once and read-once streams use non-temporal accesses, which measured
+// faster on gfx950 than cached ones for every mover.
 #include "moonep_internal.hpp"
 
 namespace moonep {
 
-// buf[slot_of[n]] = x[n div K].  One thread per (token, 16-byte vector).
-__global__ __launch_bounds__(kBlock) void dispatch_kernel(const u32x4 *__restrict__ x,
-                                                          const int32_t *__restrict__ slot_of,
-                                                          u32x4 *__restrict__ buf, int64_t total,
-                                                          int32_t V, int32_t K, uint32_t nrows)
+namespace {
+
+constexpr int KC = 8;  // experts per token handled per pass (registers)
+
+// Largest workgroup size in {256, 128, 64} that divides V (64 if none).
+inline int block_for(int32_t V)
 {
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i >= total)
+    if (V % 256 == 0)
+        return 256;
+    if (V % 128 == 0)
+        return 128;
+    return 64;
+}
+
+}  // namespace
+
+// Expert ids of one token, as uniform loads.  KT > 0: K = KT is known at
+// compile time (one wide scalar load); KT == 0: runtime K, read in chunks of
+// KC with clamped indices and masked afterwards.
+template <int KT>
+struct Slots {
+    static constexpr int kN = KT > 0 ? KT : KC;
+    uint32_t s[kN];
+    float g[kN];
+
+    __device__ __forceinline__ void load(const int32_t *so, const float *gt, int32_t K, int32_t k0,
+                                         uint32_t nrows, bool with_gates)
+    {
+#pragma unroll
+        for (int c = 0; c < kN; ++c) {
+            const bool in = KT > 0 ? true : k0 + c < K;
+            const int32_t k = KT > 0 ? c : (in ? k0 + c : K - 1);
+            const uint32_t sk = (uint32_t)so[k];
+            const float gk = with_gates ? gt[k] : 0.0f;
+            s[c] = in && sk < nrows ? sk : 0xFFFFFFFFu;  // all-ones = skip
+            g[c] = in ? gk : 0.0f;
+        }
+    }
+
+    // True when every slot of this chunk is a real row: the stores can then go
+    // out back to back.  A branch per store would make the compiler wait for
+    // all earlier memory operations (stores included) before each one.
+    __device__ __forceinline__ bool all_valid() const
+    {
+        bool ok = true;
+#pragma unroll
+        for (int c = 0; c < kN; ++c)
+            ok = ok && s[c] != 0xFFFFFFFFu;
+        return ok;
+    }
+};
+
+// buf[slot_of[n]] = x[n div K].  Tokens run along grid x (grid-stride),
+// 16-byte columns along grid y.  slot_of and buf are deliberately not
+// __restrict__: a store to buf might then change slot_of, so each
+// destination id is re-read through the vector path (an L2 hit) after the
+// previous store, and since stores and vector loads retire in order, waiting
+// for that id also waits for the previous store.  A thread thus keeps one row
+// store in flight, spaced by one L2 round trip.  On the expert-grouped write
+// pattern this measured about 10% faster on gfx950 than issuing all K stores
+// back to back, and much faster than spacing them by an uncached read.
+__global__ __launch_bounds__(kBlock) void dispatch_kernel(const u32x4 *__restrict__ x,
+                                                          const int32_t *slot_of, u32x4 *buf,
+                                                          int64_t N, int32_t V, int32_t K,
+                                                          uint32_t nrows)
+{
+    const int32_t v = (int32_t)(blockIdx.y * blockDim.x + threadIdx.x);
+    if (v >= V)
         return;
-    const int64_t tok = i / V;
-    const int64_t v = i - tok * V;
-    const u32x4 val = load_nt(x + i);
-    const int32_t *so = slot_of + tok * K;
-    for (int k = 0; k < K; ++k) {
-        const uint32_t s = (uint32_t)so[k];
-        if (s < nrows)
-            store_nt(buf + (int64_t)s * V + v, val);
+    for (int64_t tok = blockIdx.x; tok < N; tok += gridDim.x) {
+        const u32x4 val = load_nt(x + tok * V + v);
+        const int32_t *so = slot_of + tok * K;
+        for (int32_t k = 0; k < K; ++k) {
+            const uint32_t sk = (uint32_t)so[k];
+            if (sk < nrows)
+                store_nt(buf + (int64_t)sk * V + v, val);
+        }
     }
 }
 
 // y[t] = bf16(sum_k g * out[slot]) with an fp32 fused multiply-add chain in
-// ascending k, starting from +0.
+// ascending k, starting from +0; out-of-range slots contribute nothing.
+template <int KT>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const u32x4 *__restrict__ out,
                                                          const float *__restrict__ gates,
                                                          const int32_t *__restrict__ slot_of,
-                                                         u32x4 *__restrict__ y, int64_t total,
-                                                         int32_t V, int32_t K, uint32_t nrows)
+                                                         u32x4 *__restrict__ y, int32_t V,
+                                                         int32_t K, uint32_t nrows)
 {
-    constexpr int KC = 8;
-    const int64_t i = (int64_t)blockIdx.x * kBlock + threadIdx.x;
-    if (i >= total)
-        return;
-    const int64_t tok = i / V;
-    const int64_t v = i - tok * V;
-    float acc[8];
+    const int64_t tok = blockIdx.x;
+    const int32_t *so = slot_of + tok * K;
+    const float *gt = gates + tok * K;
+    constexpr int kN = Slots<KT>::kN;
+    for (int32_t v = (int32_t)threadIdx.x; v < V; v += (int32_t)blockDim.x) {
+        float acc[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        acc[j] = 0.0f;
-    for (int k0 = 0; k0 < K; k0 += KC) {
-        u32x4 vals[KC];
-        float g[KC];
-        bool use[KC];
+        for (int j = 0; j < 8; ++j)
+            acc[j] = 0.0f;
+        for (int32_t k0 = 0; k0 < K; k0 += kN) {
+            Slots<KT> sl;
+            sl.load(so, gt, K, k0, nrows, true);
+            u32x4 o[kN];
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            const int k = k0 + c;
-            use[c] = false;
-            g[c] = 0.0f;
-            vals[c] = u32x4{0, 0, 0, 0};
-            if (k < K) {
-                const uint32_t s = (uint32_t)slot_of[tok * K + k];
-                g[c] = gates[tok * K + k];
-                use[c] = s < nrows;
-                if (use[c])
-                    vals[c] = load_nt(out + (int64_t)s * V + v);
+            for (int c = 0; c < kN; ++c)
+                o[c] = load_nt(out + (int64_t)(sl.s[c] != 0xFFFFFFFFu ? sl.s[c] : 0u) * V + v);
+#pragma unroll
+            for (int c = 0; c < kN; ++c) {
+                const bool use = sl.s[c] != 0xFFFFFFFFu;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float a0 = __builtin_fmaf(sl.g[c], bf16_lo(o[c][j]), acc[2 * j]);
+                    const float a1 = __builtin_fmaf(sl.g[c], bf16_hi(o[c][j]), acc[2 * j + 1]);
+                    acc[2 * j] = use ? a0 : acc[2 * j];
+                    acc[2 * j + 1] = use ? a1 : acc[2 * j + 1];
+                }
             }
         }
+        u32x4 r;
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            if (!use[c])
-                continue;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                acc[2 * j] = __builtin_fmaf(g[c], bf16_lo(vals[c][j]), acc[2 * j]);
-                acc[2 * j + 1] = __builtin_fmaf(g[c], bf16_hi(vals[c][j]), acc[2 * j + 1]);
-            }
-        }
+        for (int j = 0; j < 4; ++j)
+            r[j] = pack_bf16(acc[2 * j], acc[2 * j + 1]);
+        store_nt(y + tok * V + v, r);
     }
-    u32x4 r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-        r[j] = pack_bf16(acc[2 * j], acc[2 * j + 1]);
-    store_nt(y + i, r);
 }
 
 // d_out[slot_of[n]] = bf16(g_n * dy[tok]) (exact product, one rounding);
-// d_gates[n] = <dy[tok], out[slot_of[n]]> in fp32.  One wave per token; each
-// lane walks the row in 16-byte steps, then the wave reduces the K dots.
+// d_gates[n] = <dy[tok], out[slot_of[n]]> in fp32: per-thread partial dots
+// over its columns, then a wave butterfly and a cross-wave sum in LDS.
+template <int KT>
 __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(
     const u32x4 *__restrict__ dy, const u32x4 *__restrict__ out, const float *__restrict__ gates,
     const int32_t *__restrict__ slot_of, u32x4 *__restrict__ d_out, float *__restrict__ d_gates,
-    int64_t N, int32_t V, int32_t K, uint32_t nrows)
+    int32_t V, int32_t K, uint32_t nrows)
 {
-    constexpr int KC = 8;
-    const int64_t tok = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
-    if (tok >= N)
-        return;
+    constexpr int kN = Slots<KT>::kN;
+    __shared__ float red[kN][kWaves];
+    const int64_t tok = blockIdx.x;
+    const int32_t *so = slot_of + tok * K;
+    const float *gt = gates + tok * K;
     const int lane = lane_id();
-    for (int k0 = 0; k0 < K; k0 += KC) {
-        uint32_t s[KC];
-        float g[KC], dot[KC];
-        bool use[KC];
+    const int wid = (int)threadIdx.x >> 6;
+    const int nw = (int)blockDim.x >> 6;
+    for (int32_t k0 = 0; k0 < K; k0 += kN) {
+        Slots<KT> sl;
+        sl.load(so, gt, K, k0, nrows, true);
+        const bool all = sl.all_valid();
+        float dot[kN];
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
-            const int k = k0 + c;
-            s[c] = 0;
-            g[c] = 0.0f;
+        for (int c = 0; c < kN; ++c)
             dot[c] = 0.0f;
-            use[c] = false;
-            if (k < K) {
-                s[c] = (uint32_t)slot_of[tok * K + k];
-                g[c] = gates[tok * K + k];
-                use[c] = s[c] < nrows;
-            }
-        }
-        for (int64_t v = lane; v < V; v += 64) {
+        for (int32_t v = (int32_t)threadIdx.x; v < V; v += (int32_t)blockDim.x) {
             const u32x4 d = load_nt(dy + tok * V + v);
+            u32x4 o[kN];
+#pragma unroll
+            for (int c = 0; c < kN; ++c)
+                o[c] = load_nt(out + (int64_t)(sl.s[c] != 0xFFFFFFFFu ? sl.s[c] : 0u) * V + v);
             float df[8];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -129,46 +184,94 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(
                 df[2 * j + 1] = bf16_hi(d[j]);
             }
 #pragma unroll
-            for (int c = 0; c < KC; ++c) {
-                if (!use[c])
-                    continue;
-                const int64_t row = (int64_t)s[c] * V + v;
-                const u32x4 o = load_nt(out + row);
-                u32x4 r;
+            for (int c = 0; c < kN; ++c) {
+                float t = dot[c];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    dot[c] = __builtin_fmaf(df[2 * j], bf16_lo(o[j]), dot[c]);
-                    dot[c] = __builtin_fmaf(df[2 * j + 1], bf16_hi(o[j]), dot[c]);
-                    r[j] = bf16_of_exact_product(g[c], df[2 * j]) |
-                           (bf16_of_exact_product(g[c], df[2 * j + 1]) << 16);
+                    t = __builtin_fmaf(df[2 * j], bf16_lo(o[c][j]), t);
+                    t = __builtin_fmaf(df[2 * j + 1], bf16_hi(o[c][j]), t);
                 }
-                store_nt(d_out + row, r);
+                dot[c] = sl.s[c] != 0xFFFFFFFFu ? t : 0.0f;
+            }
+            u32x4 r[kN];
+#pragma unroll
+            for (int c = 0; c < kN; ++c)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    r[c][j] = bf16_of_exact_product(sl.g[c], df[2 * j]) |
+                              (bf16_of_exact_product(sl.g[c], df[2 * j + 1]) << 16);
+            if (all) {
+#pragma unroll
+                for (int c = 0; c < kN; ++c)
+                    store_nt(d_out + (int64_t)sl.s[c] * V + v, r[c]);
+            } else {
+#pragma unroll
+                for (int c = 0; c < kN; ++c)
+                    if (sl.s[c] != 0xFFFFFFFFu)
+                        store_nt(d_out + (int64_t)sl.s[c] * V + v, r[c]);
             }
         }
 #pragma unroll
-        for (int c = 0; c < KC; ++c) {
+        for (int c = 0; c < kN; ++c) {
             float t = dot[c];
 #pragma unroll
             for (int m = 32; m > 0; m >>= 1)
                 t += __shfl_xor(t, m, 64);
-            if (lane == 0 && k0 + c < K)
-                d_gates[tok * K + k0 + c] = t;
+            if (lane == 0)
+                red[c][wid] = t;
         }
+        __syncthreads();
+        if ((int)threadIdx.x < kN && k0 + (int)threadIdx.x < K) {
+            float t = 0.0f;
+            for (int w = 0; w < nw; ++w)
+                t += red[threadIdx.x][w];
+            d_gates[tok * K + k0 + threadIdx.x] = t;
+        }
+        __syncthreads();
     }
+}
+
+// Instantiations for the usual top-k values; any other K takes the generic
+// runtime-K path.
+#define MOONEP_BY_K(K, F, ...)                                                   \
+    switch (K) {                                                                  \
+    case 1: F<1>(__VA_ARGS__); break;                                             \
+    case 2: F<2>(__VA_ARGS__); break;                                             \
+    case 4: F<4>(__VA_ARGS__); break;                                             \
+    case 6: F<6>(__VA_ARGS__); break;                                             \
+    case 8: F<8>(__VA_ARGS__); break;                                             \
+    default: F<0>(__VA_ARGS__); break;                                            \
+    }
+
+template <int KT>
+void run_combine(dim3 g, dim3 b, hipStream_t st, const u32x4 *out, const float *gates,
+                 const int32_t *so, u32x4 *y, int32_t V, int32_t K, uint32_t nrows)
+{
+    hipLaunchKernelGGL(combine_kernel<KT>, g, b, 0, st, out, gates, so, y, V, K, nrows);
+}
+
+template <int KT>
+void run_combine_bwd(dim3 g, dim3 b, hipStream_t st, const u32x4 *dy, const u32x4 *out,
+                     const float *gates, const int32_t *so, u32x4 *d_out, float *d_gates, int32_t V,
+                     int32_t K, uint32_t nrows)
+{
+    hipLaunchKernelGGL(combine_bwd_kernel<KT>, g, b, 0, st, dy, out, gates, so, d_out, d_gates, V,
+                       K, nrows);
 }
 
 int launch_dispatch(const moonep_shape &s, const uint16_t *x, const int32_t *slot_of, uint16_t *buf,
                     hipStream_t st)
 {
     const int64_t N = (int64_t)s.R * s.S;
-    const int32_t V = s.H / 8;
-    const int64_t total = N * V;
-    if (total == 0)
+    if (N == 0)
         return MOONEP_OK;
+    const int32_t V = s.H / 8;
     const uint32_t nrows = (uint32_t)(N * s.K);
-    const int64_t blocks = (total + kBlock - 1) / kBlock;
-    hipLaunchKernelGGL(dispatch_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, st,
-                       (const u32x4 *)x, slot_of, (u32x4 *)buf, total, V, s.K, nrows);
+    const int bs = block_for(V);
+    const uint32_t gx = (uint32_t)(N < (1 << 24) ? N : (1 << 24));
+    const uint32_t gy = (uint32_t)((V + bs - 1) / bs);
+    hipLaunchKernelGGL(dispatch_kernel, dim3(gx, gy), dim3(bs), 0, st, (const u32x4 *)x, slot_of,
+                       (u32x4 *)buf, N, V, s.K, nrows);
     return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
 }
 
@@ -176,14 +279,12 @@ int launch_combine(const moonep_shape &s, const uint16_t *out, const float *gate
                    const int32_t *slot_of, uint16_t *y, hipStream_t st)
 {
     const int64_t N = (int64_t)s.R * s.S;
-    const int32_t V = s.H / 8;
-    const int64_t total = N * V;
-    if (total == 0)
+    if (N == 0)
         return MOONEP_OK;
+    const int32_t V = s.H / 8;
     const uint32_t nrows = (uint32_t)(N * s.K);
-    const int64_t blocks = (total + kBlock - 1) / kBlock;
-    hipLaunchKernelGGL(combine_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, st,
-                       (const u32x4 *)out, gates, slot_of, (u32x4 *)y, total, V, s.K, nrows);
+    MOONEP_BY_K(s.K, run_combine, dim3((uint32_t)N), dim3(block_for(V)), st, (const u32x4 *)out,
+                gates, slot_of, (u32x4 *)y, V, s.K, nrows);
     return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
 }
 
@@ -196,10 +297,9 @@ int launch_combine_bwd(const moonep_shape &s, const uint16_t *dy, const uint16_t
         return MOONEP_OK;
     const int32_t V = s.H / 8;
     const uint32_t nrows = (uint32_t)(N * s.K);
-    const int64_t blocks = (N + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL(combine_bwd_kernel, dim3((uint32_t)blocks), dim3(kBlock), 0, st,
-                       (const u32x4 *)dy, (const u32x4 *)out, gates, slot_of, (u32x4 *)d_out,
-                       d_gates, N, V, s.K, nrows);
+    MOONEP_BY_K(s.K, run_combine_bwd, dim3((uint32_t)N), dim3(block_for(V)), st,
+                (const u32x4 *)dy, (const u32x4 *)out, gates, slot_of, (u32x4 *)d_out, d_gates, V,
+                s.K, nrows);
     return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
 }
 

@@ -119,6 +119,12 @@ EDGE = [
     synth.Workload("balanced", 8, 64, 512, 8, 64, "balanced", G=64),
     # G not a multiple of 4 (scalar reduce path)
     synth.Workload("odd_G", 4, 16, 128, 2, 64, "zipf", alpha=1.0, G=1001),
+    # top-1 routing
+    synth.Workload("k1", 2, 4, 100, 1, 64, "zipf", alpha=1.0, G=32),
+    # top-6, rows of 17 vectors
+    synth.Workload("k6", 4, 12, 50, 6, 136, "zipf", alpha=0.8, G=48),
+    # K above one pass of eight: two passes, the second partial
+    synth.Workload("k9", 4, 16, 40, 9, 64, "zipf", alpha=0.7, G=24),
 ]
 
 
