@@ -50,10 +50,14 @@ def algorithmic_bytes(R, S, K, H, G=0, reps=None):
     return d
 
 
-def source_hash():
+# Sources that define the dispatch, combine and combine_bwd kernels.
+MOVER_SOURCES = ("movers.hip", "moonep_internal.hpp")
+
+
+def source_hash(files=MOVER_SOURCES):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "load_balancing_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in sorted(files):
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode() + fh.read())
     return h.hexdigest()[:16]

@@ -14,36 +14,47 @@
 // Parallel form of the two-pointer walk: with A the running totals of the
 // spill list and B those of the deficit list, the replicas are exactly the
 // gaps between consecutive values of the union of A and B; each value's
-// place in the union comes from a binary search in the other list.  The plan
-// is O(E + R) work, so every workgroup computes it redundantly in LDS (no
-// grid-wide barrier, no second launch), workgroup 0 stores it, and then each
-// wave assigns the entries of one segment:
+// place in the union comes from a binary search in the other list.
+//
+// The plan is O(E + R) work.  Every workgroup computes it redundantly in LDS
+// (no grid-wide barrier, no second launch), with wave 0 alone doing the work
+// through wave-level scans -- 64 lanes, each owning a contiguous run of
+// experts or ranks, with no workgroup barrier until the plan is done.
+// Workgroup 0 stores it.  Then each wave assigns the entries of one segment:
 //   pos = (entries of the same expert in earlier segments)  -- from rs_scan
 //       + (entries of the same expert earlier in this segment) -- a running
 //         per-wave LDS counter plus the lane's rank among equal keys of its
-//         64-entry chunk (ballot per key bit, so time is skew-independent);
+//         64-entry chunk (ballot per key bit);
 //   pos < keep_e -> home row, else the replica whose spill range holds
-//   pos - keep_e (fixed-depth binary search).
+//   pos - keep_e (binary search of fixed depth).  Every lane computes both
+//   and selects, so the time does not depend on how much of the routing
+//   spills.
 #include "moonep_internal.hpp"
 
 namespace moonep {
 
 namespace {
 
-// LDS tables of the plan (int32).  E-sized, R-sized and cap-sized arrays.
+// LDS tables of the plan (int32).  E1 = E + 1, R1 = R + 1, CAP = E + R words.
 struct PlanLds {
-    int32_t *T, *P, *spill, *Sp, *sidx, *keep, *home_dst, *rep_first, *rep_cnt;
+    // per expert
+    int32_t *T, *P, *spill, *Sp, *sflag, *sidx, *keep, *home_dst, *rep_first, *rep_cnt;
+    // spill list (A), index i < nA
     int32_t *Aval, *Aexp, *Aexcl, *posA;
-    int32_t *load, *D, *Dp, *didx, *Bval, *Brank, *Bexcl, *Bca, *NC, *posB;
+    // per rank / deficit list (B), index j < nB
+    int32_t *load, *D, *dflag, *Dp, *didx, *Bval, *Brank, *Bexcl, *Bca, *nc, *NC, *posB;
+    // per replica (plan order)
     int32_t *U, *rai, *rbj, *rexp, *rhost, *rcnt, *rso, *rrow, *rdst;
-    int32_t *misc;  // [8]: scan scratch (kWaves) + scalars
-    int32_t *run;   // [kWaves][E]
+    int32_t *misc;  // [16]: scalars of the plan header
+    int32_t *run;   // [kWaves][E]: per-wave running counts
 };
+
+constexpr int kEArrays = 14, kRArrays = 12, kCArrays = 9;
 
 __host__ __device__ inline size_t plan_lds_words(int32_t E, int32_t R)
 {
     const size_t e1 = (size_t)E + 1, r1 = (size_t)R + 1, cap = (size_t)E + R;
-    return 13 * e1 + 10 * r1 + 9 * cap + 16 + (size_t)kWaves * E;
+    return kEArrays * e1 + kRArrays * r1 + kCArrays * cap + 16 + (size_t)kWaves * E;
 }
 
 __device__ inline PlanLds carve(int32_t *base, int32_t E, int32_t R)
@@ -51,20 +62,21 @@ __device__ inline PlanLds carve(int32_t *base, int32_t E, int32_t R)
     PlanLds L;
     const int32_t e1 = E + 1, r1 = R + 1, cap = E + R;
     int32_t *p = base;
-    int32_t **e_arrays[] = {&L.T, &L.P, &L.spill, &L.Sp, &L.sidx, &L.keep, &L.home_dst,
-                            &L.rep_first, &L.rep_cnt, &L.Aval, &L.Aexp, &L.Aexcl, &L.posA};
+    int32_t **e_arrays[kEArrays] = {&L.T, &L.P, &L.spill, &L.Sp, &L.sflag, &L.sidx, &L.keep,
+                                    &L.home_dst, &L.rep_first, &L.rep_cnt, &L.Aval, &L.Aexp,
+                                    &L.Aexcl, &L.posA};
     for (int32_t **a : e_arrays) {
         *a = p;
         p += e1;
     }
-    int32_t **r_arrays[] = {&L.load, &L.D, &L.Dp, &L.didx, &L.Bval, &L.Brank, &L.Bexcl, &L.Bca,
-                            &L.NC, &L.posB};
+    int32_t **r_arrays[kRArrays] = {&L.load, &L.D, &L.dflag, &L.Dp, &L.didx, &L.Bval,
+                                    &L.Brank, &L.Bexcl, &L.Bca, &L.nc, &L.NC, &L.posB};
     for (int32_t **a : r_arrays) {
         *a = p;
         p += r1;
     }
-    int32_t **c_arrays[] = {&L.U, &L.rai, &L.rbj, &L.rexp, &L.rhost, &L.rcnt, &L.rso, &L.rrow,
-                            &L.rdst};
+    int32_t **c_arrays[kCArrays] = {&L.U, &L.rai, &L.rbj, &L.rexp, &L.rhost, &L.rcnt, &L.rso,
+                                    &L.rrow, &L.rdst};
     for (int32_t **a : c_arrays) {
         *a = p;
         p += cap;
@@ -75,69 +87,101 @@ __device__ inline PlanLds carve(int32_t *base, int32_t E, int32_t R)
     return L;
 }
 
-// Exclusive scan of in[0..n) into out[0..n] (out[n] = total), whole block.
-__device__ void scan_array(const int32_t *in, int32_t *out, int n, int32_t *scratch)
+// Exclusive scan across the 64 lanes of a wave; *total = sum of all lanes.
+__device__ inline int wave_excl_scan(int v, int *total)
 {
-    const int per = (n + kBlock - 1) / kBlock;
-    const int first = (int)threadIdx.x * per;
+    const int lane = lane_id();
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d)
+            incl += o;
+    }
+    *total = __shfl(incl, 63, 64);
+    return incl - v;
+}
+
+__device__ inline int wave_max(int v)
+{
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) {
+        const int o = __shfl_xor(v, d, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// One wave: exclusive scan of in[0..n) into out[0..n], out[n] = total.  Lane
+// l owns the contiguous run [l*per, (l+1)*per).  Returns the total.
+__device__ int wave_scan_array(const int32_t *in, int32_t *out, int n)
+{
+    const int lane = lane_id();
+    const int per = (n + 63) / 64;
+    const int first = lane * per;
     int sum = 0;
     for (int i = 0; i < per; ++i)
         if (first + i < n)
             sum += in[first + i];
     int total = 0;
-    int run = block_exclusive_scan(sum, scratch, &total);
+    int run = wave_excl_scan(sum, &total);
     for (int i = 0; i < per; ++i)
         if (first + i < n) {
             const int v = in[first + i];
             out[first + i] = run;
             run += v;
         }
-    if (threadIdx.x == 0)
+    if (lane == 0)
         out[n] = total;
-    __syncthreads();
+    wave_sync();
+    return total;
 }
 
-// Number of values of the strictly increasing a[0..n) below x.
-__device__ inline int count_below_sorted(const int32_t *a, int n, int32_t x)
+// Number of values of the strictly increasing a[0..n) below x, with a fixed
+// number of steps (2^steps > every n this is called with), so that the time
+// does not depend on n.
+__device__ inline int count_below_sorted(const int32_t *a, int n, int32_t x, int steps)
 {
-    int lo = 0, hi = n;
-    while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (a[mid] < x)
-            lo = mid + 1;
-        else
-            hi = mid;
+    int c = 0;  // a[0..c) < x
+    for (int st = steps; st >= 0; --st) {
+        const int t = c + (1 << st);
+        const bool in = t <= n;
+        const bool below = in && a[(in ? t : 1) - 1] < x;
+        c = below ? t : c;
     }
-    return lo;
+    return c;
 }
 
-}  // namespace
-
-__global__ __launch_bounds__(kBlock) void plan_slots_kernel(
-    const int32_t *__restrict__ topk, const int32_t *__restrict__ counts,
-    const int32_t *__restrict__ seg_base, int64_t nk, int32_t R, int32_t E, int32_t C,
-    int32_t segw, int32_t nseg, int32_t nbits, int32_t search_steps, int32_t *__restrict__ plan,
-    int32_t *__restrict__ slot_of, int32_t *__restrict__ src_of_slot)
+__host__ __device__ inline int ceil_log2(int v)
 {
-    extern __shared__ int32_t lds[];
-    const PlanLds S = carve(lds, E, R);
-    const int tid = (int)threadIdx.x;
+    int b = 0;
+    while ((1 << b) < v)
+        ++b;
+    return b;
+}
+
+// The whole plan, computed by one wave into the LDS tables.
+__device__ void wave_plan(const PlanLds &S, const int32_t *__restrict__ counts, int32_t R,
+                          int32_t E, int32_t C)
+{
+    const int lane = lane_id();
     const int32_t Lx = E / R;
     const int32_t cap = E + R;
 
-    // ---- loads and whole-expert spill -----------------------------------
-    for (int e = tid; e < E; e += kBlock)
+    // rank loads before balancing
+    for (int e = lane; e < E; e += 64)
         S.T[e] = counts[e];
-    __syncthreads();
-    scan_array(S.T, S.P, E, S.misc);
-    for (int r = tid; r < R; r += kBlock) {
+    wave_sync();
+    wave_scan_array(S.T, S.P, E);
+    for (int r = lane; r < R; r += 64) {
         const int32_t ld = S.P[(r + 1) * Lx] - S.P[r * Lx];
         S.load[r] = ld;
         S.D[r] = ld < C ? C - ld : 0;
-        S.Bca[r] = ld < C ? 1 : 0;  // deficit flag, reused below
+        S.dflag[r] = ld < C ? 1 : 0;
     }
-    __syncthreads();
-    for (int e = tid; e < E; e += kBlock) {
+    wave_sync();
+    // whole-expert spill of overfull ranks, lowest expert id first
+    for (int e = lane; e < E; e += 64) {
         const int32_t r = e / Lx;
         const int32_t excess = S.load[r] - C;
         int32_t give = 0;
@@ -148,18 +192,16 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
         }
         S.spill[e] = give;
         S.keep[e] = S.T[e] - give;
-        S.posA[e] = give > 0 ? 1 : 0;  // spill flag, overwritten later
+        S.sflag[e] = give > 0 ? 1 : 0;
     }
-    __syncthreads();
-    scan_array(S.spill, S.Sp, E, S.misc);
-    scan_array(S.posA, S.sidx, E, S.misc);
-    scan_array(S.D, S.Dp, R, S.misc);
-    scan_array(S.Bca, S.didx, R, S.misc);
-    const int nA = S.sidx[E];
-    const int nB = S.didx[R];
+    wave_sync();
+    wave_scan_array(S.spill, S.Sp, E);
+    const int nA = wave_scan_array(S.sflag, S.sidx, E);
+    wave_scan_array(S.D, S.Dp, R);
+    const int nB = wave_scan_array(S.dflag, S.didx, R);
 
-    // ---- compact the spill (A) and deficit (B) lists --------------------
-    for (int e = tid; e < E; e += kBlock) {
+    // compact the spill (A) and deficit (B) lists
+    for (int e = lane; e < E; e += 64) {
         const int32_t r = e / Lx;
         if (S.spill[e] > 0) {
             const int i = S.sidx[e];
@@ -172,38 +214,48 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
         S.rep_first[e] = 0;
         S.rep_cnt[e] = 0;
     }
-    for (int r = tid; r < R; r += kBlock)
+    for (int r = lane; r < R; r += 64)
         if (S.D[r] > 0) {
             const int j = S.didx[r];
             S.Bval[j] = S.Dp[r] + S.D[r];
             S.Brank[j] = r;
             S.Bexcl[j] = S.Dp[r];
         }
-    __syncthreads();
+    wave_sync();
 
-    // ---- deficit totals that coincide with a spill total ------------------
-    for (int j = tid; j < nB; j += kBlock) {
-        const int a = count_below_sorted(S.Aval, nA, S.Bval[j]);
+    // The loops below run over all E (or R) slots with the list length as a
+    // predicate, and the searches have fixed depth: the plan takes the same
+    // time however many experts spill.
+    const int ea = ceil_log2(E + 1), rb = ceil_log2(R + 1);
+
+    // deficit totals that coincide with a spill total
+    for (int j = lane; j < R; j += 64) {
+        const bool live = j < nB;
+        const int a = count_below_sorted(S.Aval, nA, live ? S.Bval[j] : 0, ea);
         S.Bca[j] = a;
-        S.D[j] = (a < nA && S.Aval[a] == S.Bval[j]) ? 0 : 1;  // 1 = not shared with A
+        S.nc[j] = live && !(a < nA && S.Aval[a] == S.Bval[j]) ? 1 : 0;  // 1 = not shared with A
     }
-    __syncthreads();
-    scan_array(S.D, S.NC, nB, S.misc);
-    const int n_rep = nA + S.NC[nB];
+    wave_sync();
+    const int n_rep = nA + wave_scan_array(S.nc, S.NC, R);
 
-    // ---- place every boundary of the union ------------------------------
-    for (int i = tid; i < nA; i += kBlock) {
-        const int cb = count_below_sorted(S.Bval, nB, S.Aval[i]);
-        const int pos = i + S.NC[cb];
-        S.U[pos] = S.Aval[i];
-        S.rai[pos] = i;
-        S.rbj[pos] = cb;
-        S.posA[i] = pos;
+    // place every boundary of the union
+    for (int i = lane; i < E; i += 64) {
+        const bool live = i < nA;
+        const int cb = count_below_sorted(S.Bval, nB, live ? S.Aval[i] : 0, rb);
+        if (live) {
+            const int pos = i + S.NC[cb];
+            S.U[pos] = S.Aval[i];
+            S.rai[pos] = i;
+            S.rbj[pos] = cb;
+            S.posA[i] = pos;
+        }
     }
-    __syncthreads();
-    for (int j = tid; j < nB; j += kBlock) {
+    wave_sync();
+    for (int j = lane; j < R; j += 64) {
+        if (j >= nB)
+            continue;
         int pos;
-        if (S.D[j]) {
+        if (S.nc[j]) {
             pos = S.Bca[j] + S.NC[j];
             S.U[pos] = S.Bval[j];
             S.rai[pos] = S.Bca[j];
@@ -213,10 +265,10 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
         }
         S.posB[j] = pos;
     }
-    __syncthreads();
+    wave_sync();
 
-    // ---- replicas, per-expert and per-rank ranges ------------------------
-    for (int m = tid; m < cap; m += kBlock) {
+    // replicas, per-expert ranges, header scalars
+    for (int m = lane; m < cap; m += 64) {
         if (m < n_rep) {
             const int32_t lo = m ? S.U[m - 1] : 0;
             const int i = S.rai[m], j = S.rbj[m];
@@ -236,41 +288,73 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
             S.rdst[m] = 0;
         }
     }
-    for (int i = tid; i < nA; i += kBlock) {
+    for (int i = lane; i < E; i += 64) {
+        if (i >= nA)
+            continue;
         const int e = S.Aexp[i];
         const int f = i ? S.posA[i - 1] + 1 : 0;
         S.rep_first[e] = f;
         S.rep_cnt[e] = S.posA[i] - f + 1;
     }
-    if (tid < 8)
-        S.misc[8 + tid] = 0;
-    __syncthreads();
-    for (int j = tid; j < nB; j += kBlock) {
+    int most = 0;
+    for (int j = lane; j < R; j += 64) {
+        if (j >= nB)
+            continue;
         const int f = j ? S.posB[j - 1] + 1 : 0;
-        atomicMax(&S.misc[8], S.posB[j] - f + 1);  // most replicas on one rank
+        const int c = S.posB[j] - f + 1;  // replicas hosted by this rank
+        most = c > most ? c : most;
     }
-    for (int e = tid; e < E; e += kBlock)
-        atomicMax(&S.misc[9], S.T[e]);
+    int tmax = 0;
+    for (int e = lane; e < E; e += 64)
+        tmax = S.T[e] > tmax ? S.T[e] : tmax;
+    most = wave_max(most);
+    tmax = wave_max(tmax);
+    if (lane == 0) {
+        S.misc[MOONEP_PLAN_H_N_REP] = n_rep;
+        S.misc[MOONEP_PLAN_H_N_SPILL] = nA;
+        S.misc[MOONEP_PLAN_H_N_DEFICIT] = nB;
+        S.misc[MOONEP_PLAN_H_MAX_REP_RANK] = most;
+        S.misc[MOONEP_PLAN_H_TMAX] = tmax;
+        S.misc[MOONEP_PLAN_H_C] = C;
+        S.misc[MOONEP_PLAN_H_L] = Lx;
+        S.misc[MOONEP_PLAN_H_CAP] = cap;
+        for (int h = 8; h < 16; ++h)
+            S.misc[h] = 0;
+    }
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(kBlock) void plan_slots_kernel(
+    const int32_t *__restrict__ topk, const int32_t *__restrict__ counts,
+    const int32_t *__restrict__ seg_base, int64_t nk, int32_t R, int32_t E, int32_t C,
+    int32_t segw, int32_t nseg, int32_t nbits, int32_t search_steps, int32_t *__restrict__ plan,
+    int32_t *__restrict__ slot_of, int32_t *__restrict__ src_of_slot)
+{
+    extern __shared__ int32_t lds[];
+    const PlanLds S = carve(lds, E, R);
+    const int tid = (int)threadIdx.x;
+    const int wid = tid >> 6;
+    const int lane = lane_id();
+    const int32_t seg = (int32_t)blockIdx.x * kWaves + wid;
+    const int32_t cap = E + R;
+
+    // Waves other than 0 fetch their segment's bases while wave 0 plans.
+    int32_t *run = S.run + wid * E;
+    if (seg < nseg)
+        for (int e = lane; e < E; e += 64)
+            run[e] = seg_base[(int64_t)e * nseg + seg];
+    if (wid == 0)
+        wave_plan(S, counts, R, E, C);
     __syncthreads();
 
     // ---- workgroup 0 stores the plan --------------------------------------
     if (blockIdx.x == 0) {
         const PlanLayout pl = plan_layout(E, R);
-        if (tid < 16) {
-            int32_t v = 0;
-            switch (tid) {
-            case MOONEP_PLAN_H_N_REP: v = n_rep; break;
-            case MOONEP_PLAN_H_N_SPILL: v = nA; break;
-            case MOONEP_PLAN_H_N_DEFICIT: v = nB; break;
-            case MOONEP_PLAN_H_MAX_REP_RANK: v = S.misc[8]; break;
-            case MOONEP_PLAN_H_TMAX: v = S.misc[9]; break;
-            case MOONEP_PLAN_H_C: v = C; break;
-            case MOONEP_PLAN_H_L: v = Lx; break;
-            case MOONEP_PLAN_H_CAP: v = cap; break;
-            default: v = 0;
-            }
-            plan[pl.header + tid] = v;
-        }
+        if (tid < 16)
+            plan[pl.header + tid] = S.misc[tid];
+        const int nA = S.misc[MOONEP_PLAN_H_N_SPILL];
+        const int nB = S.misc[MOONEP_PLAN_H_N_DEFICIT];
         for (int m = tid; m < cap; m += kBlock) {
             plan[pl.rep_expert + m] = S.rexp[m];
             plan[pl.rep_host + m] = S.rhost[m];
@@ -279,7 +363,7 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
             plan[pl.rep_row_off + m] = S.rrow[m];
         }
         for (int e = tid; e < E; e += kBlock) {
-            const int32_t r = e / Lx;
+            const int32_t r = e / (E / R);
             plan[pl.spill + e] = S.spill[e];
             plan[pl.keep + e] = S.keep[e];
             plan[pl.home_row_off + e] = S.home_dst[e] - r * C;
@@ -301,15 +385,8 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
     }
 
     // ---- slot assignment: one wave per segment -----------------------------
-    const int wid = tid >> 6;
-    const int lane = lane_id();
-    const int32_t seg = (int32_t)blockIdx.x * kWaves + wid;
     if (seg >= nseg)
         return;
-    int32_t *run = S.run + wid * E;
-    for (int e = lane; e < E; e += 64)
-        run[e] = seg_base[(int64_t)e * nseg + seg];
-    wave_sync();
     const int64_t beg = (int64_t)seg * segw;
     const int64_t end = beg + segw < nk ? beg + segw : nk;
     for (int64_t b0 = beg; b0 < end; b0 += 64 * kChunkBatch) {
@@ -338,22 +415,20 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
             if (ok && (same >> lane) == 1ull)
                 run[ee] = pos + 1;  // the highest lane of a group holds its last position
             wave_sync();
-            int32_t dst;
+            // home destination and replica destination, both computed
             const int32_t kp = S.keep[ee];
-            if (pos < kp) {
-                dst = S.home_dst[ee] + pos;
-            } else {
-                const int32_t q = pos - kp;
-                const int32_t f = S.rep_first[ee];
-                const int32_t last = f + S.rep_cnt[ee] - 1;
-                int32_t j = f;
-                for (int st = search_steps; st >= 0; --st) {
-                    const int32_t t = j + (1 << st);
-                    if (t <= last && S.rso[t] <= q)
-                        j = t;
-                }
-                dst = S.rdst[j] + q;
+            const int32_t home = S.home_dst[ee] + pos;
+            const int32_t q = pos - kp;
+            const int32_t f = S.rep_first[ee];
+            const int32_t last = f + S.rep_cnt[ee] - 1;
+            int32_t j = f;
+            for (int st = search_steps; st >= 0; --st) {
+                const int32_t t = j + (1 << st);
+                const int32_t tt = t <= last ? t : last;  // keep the read in the table
+                const bool step = t <= last && S.rso[tt < 0 ? 0 : tt] <= q;
+                j = step ? t : j;
             }
+            const int32_t dst = pos < kp ? home : S.rdst[j] + q;
             // dst is in range whenever counts match topk; the check keeps a
             // mismatched call from writing outside src_of_slot.
             if (ok && (uint64_t)(uint32_t)dst < (uint64_t)nk) {

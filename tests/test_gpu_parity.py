@@ -203,3 +203,35 @@ def test_plan_with_several_chunk_batches_per_wave():
     compare_plan(b.plan_fields(), pl, w.E, w.R)
     np.testing.assert_array_equal(b.slot_of.cpu().numpy(), slot_of)
     np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot)
+
+
+def test_plan_random_shapes():
+    """Plan, counts, maxvio and slot maps on 300 random small shapes (skews
+    from uniform to one hot expert), bit-exact against the oracle."""
+    rng = np.random.default_rng(11)
+    for case in range(300):
+        R = int(rng.integers(1, 17))
+        L = int(rng.integers(1, 9))
+        E = R * L
+        K = int(rng.integers(1, min(E, 8) + 1))
+        S = int(rng.integers(0, 60))
+        N = R * S
+        skew = rng.uniform(0, 3)
+        p = (np.arange(E) + 1.0) ** -skew
+        p = p[rng.permutation(E)]
+        p /= p.sum()
+        topk = np.concatenate([rng.choice(E, size=K, replace=False, p=p) for _ in range(N)]
+                              ).astype(np.int32) if N else np.zeros(0, dtype=np.int32)
+        w = synth.Workload(f"rand{case}", R, E, S, K, 8, "zipf")
+        T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk)
+        s = shape_of(w)
+        b = mx.allocate(s)
+        mx.plan_step(b, to_dev(topk) if N else torch.empty(0, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        msg = f"case {case}: R={R} E={E} S={S} K={K}"
+        np.testing.assert_array_equal(b.expert_counts.cpu().numpy(), T, err_msg=msg)
+        assert b.maxvio.item() == mv, msg
+        compare_plan(b.plan_fields(), pl, E, R)
+        if N:
+            np.testing.assert_array_equal(b.slot_of.cpu().numpy(), slot_of, err_msg=msg)
+            np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot, err_msg=msg)
