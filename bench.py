@@ -18,7 +18,15 @@ per call (what the call must move at least):
 Also printed: per-call microseconds, plan latency per maxvio level, the
 roofline of the dominant kernel, and the CPU oracle timed on every level.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+Other workloads (same step, one routing each): --workload dsv3 (R=32, E=256,
+S=4096, K=8, H=7168, Zipf 1.2, weight-gradients 7168 x 2048) and --workload
+adversarial (R=16, E=128, S=8192, K=8, H=4096, every token to experts 0..7).
+Their multi-GB gradient arrays repeat eight seeded synthetic rows (the
+reduction's time does not depend on the values); their CPU baseline runs the
+oracle's dispatch and combine on a sample of tokens.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload sweep]
+                    [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -35,6 +43,14 @@ CALLS = ("route_stats", "plan", "dispatch", "combine", "combine_bwd", "replica_g
 KERNEL_OF = {"dispatch": "dispatch_kernel", "combine": "combine_kernel",
              "combine_bwd": "combine_bwd_kernel", "replica_grad_reduce": "replica_reduce_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sweep.json")
+WORKLOAD_NAME = {
+    "sweep": "maxvio sweep R8 E64 S4096 K8 H2048, maxvio 0/0.5/1/2/4 cycled per step; "
+             "backward weight-grads 2048x1408 fp32",
+    "dsv3": "DeepSeek-V3-like R32 E256 S4096 K8 H7168, Zipf 1.2; backward weight-grads "
+            "7168x2048 fp32",
+    "adversarial": "adversarial R16 E128 S8192 K8 H4096, every token to experts 0..7, gates 1/8; "
+                   "backward weight-grads 4096x2048 fp32",
+}
 
 
 def algorithmic_bytes(R, S, K, H, G=0, reps=None):
@@ -97,12 +113,43 @@ def cpu_baseline(levels, seed):
                       f"dispatch+combine algorithmic bytes / their time"}
 
 
+def cpu_baseline_sampled(w, seed, ntok=2048):
+    """The CPU oracle, single-threaded, on dispatch and combine of a token sample."""
+    import numpy as np
+
+    import oracle
+    import synth
+
+    topk, gates = synth.routing(w, seed)
+    x = synth.activations(w, seed)
+    T, _ = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
+    slot_of, src_of_slot = oracle.slots(w.R, w.E, w.S, w.K, topk, pl)
+    toks = np.random.default_rng(seed).choice(w.N, size=min(ntok, w.N), replace=False)
+    ents = (toks[:, None] * w.K + np.arange(w.K)).ravel()
+    rows = slot_of[ents].astype(np.int64)
+    t0 = time.perf_counter()
+    buf_rows = oracle.dispatch_rows(w.K, w.H, x, src_of_slot, rows)
+    t1 = time.perf_counter()
+    oracle.combine(w.K, w.H, buf_rows, gates[ents], np.arange(rows.size, dtype=np.int32))
+    t2 = time.perf_counter()
+    b = algorithmic_bytes(w.R, w.S, w.K, w.H)
+    per_tok = (b["dispatch"] + b["combine"]) / w.N
+    return {"value": round(per_tok * toks.size / (t2 - t0) / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle",
+            "sample": f"dispatch and combine of {toks.size} random tokens of the workload "
+                      f"(seed {seed}), single thread: {1e3 * (t1 - t0):.1f} ms + "
+                      f"{1e3 * (t2 - t1):.1f} ms; value = their share of the algorithmic "
+                      f"bytes / time"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--workload", default="sweep", choices=("sweep", "dsv3", "adversarial"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-copy-probe", action="store_true",
                     help="skip the untimed 1 GiB copy used to calibrate HBM counters")
@@ -121,25 +168,40 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    base = synth.WORKLOADS["sweep"]
+    base = synth.WORKLOADS[args.workload]
     R, E, S, K, H, G = base.R, base.E, base.S, base.K, base.H, base.G
     N, NK = R * S, R * S * K
     s = mx.Shape(R, E, S, K, H)
-    levels = list(synth.SWEEP_LEVELS)
+    if args.workload == "sweep":
+        routings = [(f"{lv:g}", synth.sweep_workload(lv, args.seed)) for lv in synth.SWEEP_LEVELS]
+    else:
+        routings = [(args.workload, base)]
+    levels = [name for name, _ in routings]
 
     # ---- inputs, resident in HBM ------------------------------------------
     up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     topks, gatess = [], []
-    for lv in levels:
-        wl = synth.sweep_workload(lv, args.seed)
+    for _, wl in routings:
         t, g = synth.routing(wl, args.seed)
         topks.append(up(t))
         gatess.append(up(g))
     x = up(synth.activations(base, args.seed).view(np.int16)).view(torch.bfloat16)
     dy = up(synth.activations(base, args.seed, synth.TAG_DY).view(np.int16)).view(torch.bfloat16)
     cap = E + R
-    home = up(synth.normal_f32(args.seed, synth.TAG_GRAD_HOME, E * G, 0.01))
-    rep = up(synth.normal_f32(args.seed, synth.TAG_GRAD_REP, cap * G, 0.01))
+    if (E + cap) * G <= (1 << 29):
+        home = up(synth.normal_f32(args.seed, synth.TAG_GRAD_HOME, E * G, 0.01))
+        rep = up(synth.normal_f32(args.seed, synth.TAG_GRAD_REP, cap * G, 0.01))
+    else:
+        # eight seeded synthetic rows, repeated over the experts and replicas
+        pat_h = up(synth.normal_f32(args.seed, synth.TAG_GRAD_HOME, 8 * G, 0.01)).view(8, G)
+        pat_r = up(synth.normal_f32(args.seed, synth.TAG_GRAD_REP, 8 * G, 0.01)).view(8, G)
+        home = torch.empty((E, G), dtype=torch.float32, device=dev)
+        rep = torch.empty((cap, G), dtype=torch.float32, device=dev)
+        for e in range(E):
+            home[e].copy_(pat_h[e % 8])
+        for j in range(cap):
+            rep[j].copy_(pat_r[j % 8])
+        del pat_h, pat_r
     b = mx.allocate(s, dev)
     y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
     d_out = torch.empty((NK, H), dtype=torch.bfloat16, device=dev)
@@ -210,7 +272,7 @@ def main():
     dc_bytes = byt["dispatch"] + byt["combine"]
     dc_s = 1e-3 * (mean(per_call["dispatch"]) + mean(per_call["combine"]))
     value = dc_bytes / dc_s / 1e9
-    plan_us = {f"{lv:g}": round(1e3 * (mean(per_level[lv]["route_stats"]) +
+    plan_us = {lv: round(1e3 * (mean(per_level[lv]["route_stats"]) +
                                       mean(per_level[lv]["plan"])), 2)
                for lv in levels if per_level[lv]["plan"]}
     pv = list(plan_us.values())
@@ -238,7 +300,7 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-        if t.get("source_hash") == source_hash():
+        if t.get("source_hash") == source_hash() and args.workload == "sweep":
             measured = {k: v["hbm_bytes_per_launch"] for k, v in t.get("kernels", {}).items()}
     for name in kern:
         kern[name]["traffic"] = measured.get(name)
@@ -254,10 +316,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(1e3 * wall / args.steps, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "maxvio sweep R8 E64 S4096 K8 H2048, maxvio 0/0.5/1/2/4 "
-                               "cycled per step; backward weight-grads 2048x1408 fp32",
+        "config": {"workload": WORKLOAD_NAME[args.workload],
                    "R": R, "E": E, "S": S, "K": K, "H": H, "G": G,
-                   "global_batch": N, "parallelism": "1 GPU, 8 logical ranks"},
+                   "global_batch": N, "parallelism": f"1 GPU, {R} logical ranks"},
         "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "value_def": "dispatch+combine algorithmic bytes / their HIP-event time",
         "forward_GBps_incl_plan": round(dc_bytes / (1e-3 * (mean(per_call["dispatch"]) +
@@ -269,11 +330,13 @@ def main():
         "plan_spread": round((max(pv) - min(pv)) / min(pv), 4) if pv else None,
         "breakdown_us": us,
         "kernels": kern,
-        "replicas_per_level": {f"{lv:g}": int(sum(r)) for lv, r in zip(levels, reps_per_level)},
+        "replicas_per_level": {lv: int(sum(r)) for lv, r in zip(levels, reps_per_level)},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(levels, args.seed)
+        result["cpu_baseline"] = (cpu_baseline(synth.SWEEP_LEVELS, args.seed)
+                                  if args.workload == "sweep"
+                                  else cpu_baseline_sampled(base, args.seed))
     print(json.dumps(result), flush=True)
 
 

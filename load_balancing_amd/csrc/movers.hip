@@ -35,16 +35,18 @@ inline int block_for(int32_t V)
     return 64;
 }
 
-// Resident workgroups per CU that measured best on gfx950 for each mover in
-// the full step on the expert-grouped access pattern (HBM efficiency falls
-// when more scattered row requests are in flight; too few leave it idle):
-// dispatch 3, combine 2, combine_bwd 4.  Uncapped, the same kernels ran
-// 2-4% slower (combine 212 us against 198 us on the 1.2 GB sweep step).
-constexpr int kDispatchWgPerCu = 3, kCombineWgPerCu = 2, kCombineBwdWgPerCu = 4;
+// Resident waves per CU that measured best on gfx950 for each mover in the
+// full step on the expert-grouped access pattern (HBM efficiency falls when
+// more scattered row requests are in flight; too few leave it idle):
+// dispatch 12, combine 8, combine_bwd 16 -- 3, 2 and 4 workgroups of 256
+// threads.  Uncapped, the same kernels ran 2-4% slower (combine 212 us
+// against 198 us on the 1.2 GB sweep step).
+constexpr int kDispatchWaves = 12, kCombineWaves = 8, kCombineBwdWaves = 16;
 
-// Dynamic LDS a workgroup requests so that exactly `per_cu` of them fit in
-// one CU's LDS; the kernels do not use it, it only caps residency.
-size_t residency_lds(int per_cu)
+// Dynamic LDS a workgroup of `threads` requests so that only
+// waves_per_cu / (threads / 64) of them fit in one CU's LDS; the kernels do not
+// use it, it only caps residency.
+size_t residency_lds(int waves_per_cu, int threads)
 {
     static int lds_per_cu = 0;
     if (lds_per_cu == 0) {
@@ -56,8 +58,10 @@ size_t residency_lds(int per_cu)
         else
             lds_per_cu = 160 * 1024;
     }
+    int per_cu = waves_per_cu / (threads / 64);
+    per_cu = per_cu < 2 ? 2 : per_cu;
     // between lds/(per_cu+1) and lds/per_cu, away from both (and under the
-    // 64 KiB default dynamic limit for per_cu >= 2), in 256-byte units
+    // 64 KiB default dynamic limit), in 256-byte units
     const size_t b = (size_t)((double)lds_per_cu / (per_cu + 0.6));
     return b & ~(size_t)255;
 }
@@ -100,15 +104,32 @@ struct Slots {
     }
 };
 
-// buf[slot_of[n]] = x[n div K].  Tokens run along grid x (grid-stride),
-// 16-byte columns along grid y.  slot_of and buf are deliberately not
-// __restrict__: a store to buf might then change slot_of, so each
-// destination id is re-read through the vector path (an L2 hit) after the
-// previous store, and since stores and vector loads retire in order, waiting
-// for that id also waits for the previous store.  A thread thus keeps one row
-// store in flight, spaced by one L2 round trip.  On the expert-grouped write
-// pattern this measured about 10% faster on gfx950 than issuing all K stores
-// back to back, and much faster than spacing them by an uncached read.
+// buf[slot_of[n]] = x[n div K], one token row and one 16-byte column per
+// thread.  slot_of and buf are deliberately not __restrict__: a store to buf
+// might then change slot_of, so each destination id is re-read through the
+// vector path (an L2 hit) after the previous store, and since stores and
+// vector loads retire in order, waiting for that id also waits for the
+// previous store.  A thread thus keeps one row store in flight, spaced by one
+// L2 round trip.  On the expert-grouped write pattern this measured about 10%
+// faster on gfx950 than issuing all K stores back to back, and much faster
+// than spacing them by an uncached read.
+__device__ __forceinline__ void dispatch_column(const u32x4 *__restrict__ x,
+                                                const int32_t *slot_of, u32x4 *buf, int64_t tok,
+                                                int32_t V, int32_t v, int32_t K, uint32_t nrows)
+{
+    const u32x4 val = load_nt(x + tok * V + v);
+    const int32_t *so = slot_of + tok * K;
+    for (int32_t k = 0; k < K; ++k) {
+        const uint32_t sk = (uint32_t)so[k];
+        if (sk < nrows)
+            store_nt(buf + (int64_t)sk * V + v, val);
+    }
+}
+
+// Rows of one column block: tokens along grid x (grid-stride), grid y = 1.
+// (Written with the column offset blockIdx.y * blockDim.x although it is 0:
+// that form measured 2% faster on gfx950 than v = threadIdx.x, repeatably;
+// the two differ only in the scalar set-up at kernel entry.)
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(const u32x4 *__restrict__ x,
                                                           const int32_t *slot_of, u32x4 *buf,
                                                           int64_t N, int32_t V, int32_t K,
@@ -117,59 +138,99 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(const u32x4 *__restric
     const int32_t v = (int32_t)(blockIdx.y * blockDim.x + threadIdx.x);
     if (v >= V)
         return;
-    for (int64_t tok = blockIdx.x; tok < N; tok += gridDim.x) {
-        const u32x4 val = load_nt(x + tok * V + v);
-        const int32_t *so = slot_of + tok * K;
-        for (int32_t k = 0; k < K; ++k) {
-            const uint32_t sk = (uint32_t)so[k];
-            if (sk < nrows)
-                store_nt(buf + (int64_t)sk * V + v, val);
+    for (int64_t tok = blockIdx.x; tok < N; tok += gridDim.x)
+        dispatch_column(x, slot_of, buf, tok, V, v, K, nrows);
+}
+
+// Rows of several column blocks: workgroup w = t*ncb + c covers column block
+// c of token t, so the blocks of one token's rows are adjacent in launch order
+// and each row is written in one pass.
+__global__ __launch_bounds__(kBlock) void dispatch_blocks_kernel(const u32x4 *__restrict__ x,
+                                                                 const int32_t *slot_of,
+                                                                 u32x4 *buf, int64_t N, int32_t V,
+                                                                 int32_t ncb, int32_t K,
+                                                                 uint32_t nrows)
+{
+    const uint64_t total = (uint64_t)N * (uint64_t)ncb;
+    for (uint64_t w = blockIdx.x; w < total; w += gridDim.x) {
+        uint64_t tok;
+        uint32_t c;
+        if (w < 0xFFFFFFFFull) {
+            tok = (uint32_t)w / (uint32_t)ncb;
+            c = (uint32_t)w - (uint32_t)tok * (uint32_t)ncb;
+        } else {
+            tok = w / (uint64_t)ncb;
+            c = (uint32_t)(w - tok * (uint64_t)ncb);
         }
+        const int32_t v = (int32_t)(c * blockDim.x + threadIdx.x);
+        if (v < V)
+            dispatch_column(x, slot_of, buf, (int64_t)tok, V, v, K, nrows);
     }
 }
 
 // y[t] = bf16(sum_k g * out[slot]) with an fp32 fused multiply-add chain in
 // ascending k, starting from +0; out-of-range slots contribute nothing.
+// Workgroup w = t*nwb + c covers column blocks [c*cpb, (c+1)*cpb) of token t:
+// a whole row per workgroup when it is short (under 4 column blocks), one
+// column block per workgroup otherwise; both measured best in their range.
 template <int KT>
 __global__ __launch_bounds__(kBlock) void combine_kernel(const u32x4 *__restrict__ out,
                                                          const float *__restrict__ gates,
                                                          const int32_t *__restrict__ slot_of,
-                                                         u32x4 *__restrict__ y, int32_t V,
+                                                         u32x4 *__restrict__ y, int64_t N,
+                                                         int32_t V, int32_t nwb, int32_t cpb,
                                                          int32_t K, uint32_t nrows)
 {
-    const int64_t tok = blockIdx.x;
-    const int32_t *so = slot_of + tok * K;
-    const float *gt = gates + tok * K;
     constexpr int kN = Slots<KT>::kN;
-    for (int32_t v = (int32_t)threadIdx.x; v < V; v += (int32_t)blockDim.x) {
-        float acc[8];
+    const uint64_t total = (uint64_t)N * (uint64_t)nwb;
+    for (uint64_t w = blockIdx.x; w < total; w += gridDim.x) {
+        uint64_t tok;
+        uint32_t wb;
+        if (nwb == 1) {
+            tok = w;
+            wb = 0;
+        } else if (w < 0xFFFFFFFFull) {
+            tok = (uint32_t)w / (uint32_t)nwb;
+            wb = (uint32_t)w - (uint32_t)tok * (uint32_t)nwb;
+        } else {
+            tok = w / (uint64_t)nwb;
+            wb = (uint32_t)(w - tok * (uint64_t)nwb);
+        }
+        const int32_t v_end = (int32_t)((wb + 1) * cpb * blockDim.x) < V
+                                  ? (int32_t)((wb + 1) * cpb * blockDim.x) : V;
+        for (int32_t v = (int32_t)(wb * cpb * blockDim.x + threadIdx.x); v < v_end;
+             v += (int32_t)blockDim.x) {
+            const int32_t *so = slot_of + (int64_t)tok * K;
+            const float *gt = gates + (int64_t)tok * K;
+            float acc[8];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            acc[j] = 0.0f;
-        for (int32_t k0 = 0; k0 < K; k0 += kN) {
-            Slots<KT> sl;
-            sl.load(so, gt, K, k0, nrows, true);
-            u32x4 o[kN];
+            for (int j = 0; j < 8; ++j)
+                acc[j] = 0.0f;
+            for (int32_t k0 = 0; k0 < K; k0 += kN) {
+                Slots<KT> sl;
+                sl.load(so, gt, K, k0, nrows, true);
+                u32x4 o[kN];
 #pragma unroll
-            for (int c = 0; c < kN; ++c)
-                o[c] = load_nt(out + (int64_t)(sl.s[c] != 0xFFFFFFFFu ? sl.s[c] : 0u) * V + v);
+                for (int c = 0; c < kN; ++c)
+                    o[c] = load_nt(out + (int64_t)(sl.s[c] != 0xFFFFFFFFu ? sl.s[c] : 0u) * V + v);
 #pragma unroll
-            for (int c = 0; c < kN; ++c) {
-                const bool use = sl.s[c] != 0xFFFFFFFFu;
+                for (int c = 0; c < kN; ++c) {
+                    const bool use = sl.s[c] != 0xFFFFFFFFu;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float a0 = __builtin_fmaf(sl.g[c], bf16_lo(o[c][j]), acc[2 * j]);
-                    const float a1 = __builtin_fmaf(sl.g[c], bf16_hi(o[c][j]), acc[2 * j + 1]);
-                    acc[2 * j] = use ? a0 : acc[2 * j];
-                    acc[2 * j + 1] = use ? a1 : acc[2 * j + 1];
+                    for (int j = 0; j < 4; ++j) {
+                        const float a0 = __builtin_fmaf(sl.g[c], bf16_lo(o[c][j]), acc[2 * j]);
+                        const float a1 = __builtin_fmaf(sl.g[c], bf16_hi(o[c][j]), acc[2 * j + 1]);
+                        acc[2 * j] = use ? a0 : acc[2 * j];
+                        acc[2 * j + 1] = use ? a1 : acc[2 * j + 1];
+                    }
                 }
             }
-        }
-        u32x4 r;
+            u32x4 r;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            r[j] = pack_bf16(acc[2 * j], acc[2 * j + 1]);
-        store_nt(y + tok * V + v, r);
+            for (int j = 0; j < 4; ++j)
+                r[j] = pack_bf16(acc[2 * j], acc[2 * j + 1]);
+            store_nt(y + (int64_t)tok * V + v, r);
+        }
     }
 }
 
@@ -272,10 +333,11 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(
 
 template <int KT>
 void run_combine(dim3 g, dim3 b, hipStream_t st, const u32x4 *out, const float *gates,
-                 const int32_t *so, u32x4 *y, int32_t V, int32_t K, uint32_t nrows)
+                 const int32_t *so, u32x4 *y, int64_t N, int32_t V, int32_t nwb, int32_t cpb,
+                 int32_t K, uint32_t nrows)
 {
-    hipLaunchKernelGGL(combine_kernel<KT>, g, b, residency_lds(kCombineWgPerCu), st, out, gates,
-                       so, y, V, K, nrows);
+    hipLaunchKernelGGL(combine_kernel<KT>, g, b, residency_lds(kCombineWaves, (int)b.x), st, out,
+                       gates, so, y, N, V, nwb, cpb, K, nrows);
 }
 
 template <int KT>
@@ -283,7 +345,7 @@ void run_combine_bwd(dim3 g, dim3 b, hipStream_t st, const u32x4 *dy, const u32x
                      const float *gates, const int32_t *so, u32x4 *d_out, float *d_gates, int32_t V,
                      int32_t K, uint32_t nrows)
 {
-    hipLaunchKernelGGL(combine_bwd_kernel<KT>, g, b, residency_lds(kCombineBwdWgPerCu), st, dy,
+    hipLaunchKernelGGL(combine_bwd_kernel<KT>, g, b, residency_lds(kCombineBwdWaves, (int)b.x), st, dy,
                        out, gates, so, d_out, d_gates, V, K, nrows);
 }
 
@@ -296,10 +358,16 @@ int launch_dispatch(const moonep_shape &s, const uint16_t *x, const int32_t *slo
     const int32_t V = s.H / 8;
     const uint32_t nrows = (uint32_t)(N * s.K);
     const int bs = block_for(V);
-    const uint32_t gx = (uint32_t)(N < (1 << 24) ? N : (1 << 24));
-    const uint32_t gy = (uint32_t)((V + bs - 1) / bs);
-    hipLaunchKernelGGL(dispatch_kernel, dim3(gx, gy), dim3(bs), residency_lds(kDispatchWgPerCu), st,
-                       (const u32x4 *)x, slot_of, (u32x4 *)buf, N, V, s.K, nrows);
+    const int32_t ncb = (V + bs - 1) / bs;
+    const int64_t total = N * ncb;
+    const uint32_t grid = (uint32_t)(total < (1 << 24) ? total : (1 << 24));
+    const size_t lds = residency_lds(kDispatchWaves, bs);
+    if (ncb == 1)
+        hipLaunchKernelGGL(dispatch_kernel, dim3(grid, 1), dim3(bs), lds, st, (const u32x4 *)x,
+                           slot_of, (u32x4 *)buf, N, V, s.K, nrows);
+    else
+        hipLaunchKernelGGL(dispatch_blocks_kernel, dim3(grid), dim3(bs), lds, st, (const u32x4 *)x,
+                           slot_of, (u32x4 *)buf, N, V, ncb, s.K, nrows);
     return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
 }
 
@@ -311,8 +379,14 @@ int launch_combine(const moonep_shape &s, const uint16_t *out, const float *gate
         return MOONEP_OK;
     const int32_t V = s.H / 8;
     const uint32_t nrows = (uint32_t)(N * s.K);
-    MOONEP_BY_K(s.K, run_combine, dim3((uint32_t)N), dim3(block_for(V)), st, (const u32x4 *)out,
-                gates, slot_of, (u32x4 *)y, V, s.K, nrows);
+    const int bs = block_for(V);
+    const int32_t ncb = (V + bs - 1) / bs;
+    const int32_t cpb = ncb < 4 ? ncb : 1;  // column blocks per workgroup
+    const int32_t nwb = (ncb + cpb - 1) / cpb;
+    const int64_t total = N * nwb;
+    const uint32_t grid = (uint32_t)(total < (1 << 24) ? total : (1 << 24));
+    MOONEP_BY_K(s.K, run_combine, dim3(grid), dim3(bs), st, (const u32x4 *)out, gates, slot_of,
+                (u32x4 *)y, N, V, nwb, cpb, s.K, nrows);
     return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
 }
 
