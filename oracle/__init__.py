@@ -98,6 +98,8 @@ def lib():
         L.orc_forward_tokens.argtypes = [i32, i32, p, p, p, p, p, p, i64, p, p]
         L.orc_combine_bwd.restype = None
         L.orc_combine_bwd.argtypes = [i64, i32, i32, p, p, p, p, p, p]
+        L.orc_dispatch_bwd.restype = None
+        L.orc_dispatch_bwd.argtypes = [i64, i32, i32, p, p, p]
         L.orc_replica_grad_reduce.restype = None
         L.orc_replica_grad_reduce.argtypes = [i32, ctypes.POINTER(_CPlan), i64, p, p]
         L.orc_replica_grad_reduce_at.restype = None
@@ -243,6 +245,16 @@ def combine_bwd(K, H, dy, out, gates, slot_of):
     lib().orc_combine_bwd(N, K, H, _p(dy), _p(out), _p(gates), _p(slot_of), _p(d_out),
                           _p(d_gates))
     return d_out, d_gates
+
+
+def dispatch_bwd(K, H, d_buf, slot_of):
+    """dx [N, H] bf16 from the buffer gradient d_buf [N*K, H] bf16."""
+    d_buf = _c(d_buf, np.uint16)
+    slot_of = _c(slot_of, np.int32)
+    N = slot_of.size // K
+    dx = np.empty((N, H), dtype=np.uint16)
+    lib().orc_dispatch_bwd(N, K, H, _p(d_buf), _p(slot_of), _p(dx))
+    return dx
 
 
 def replica_grad_reduce(E, pl: Plan, G, home, rep):

@@ -453,6 +453,25 @@ void orc_combine_bwd(int64_t N, int32_t K, int32_t H, const uint16_t *dy, const 
 }
 
 /* ------------------------------------------------------------------------ */
+/* Step 6b: dispatch backward (training use, [NCIJ] "The core idea").        */
+/* buf[slot_of[n]] = x[n div K], so the gradient of x gathers the K rows of   */
+/* the buffer gradient:  dx[tok] = sum_k d_buf[slot_of[tok*K + k]],           */
+/* summed in fp64 in ascending k, rounded once to bf16.                       */
+/* ------------------------------------------------------------------------ */
+
+void orc_dispatch_bwd(int64_t N, int32_t K, int32_t H, const uint16_t *d_buf,
+                      const int32_t *slot_of, uint16_t *dx)
+{
+    for (int64_t t = 0; t < N; ++t)
+        for (int32_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int32_t k = 0; k < K; ++k)
+                acc += orc_bf16_to_double(d_buf[(int64_t)slot_of[t * K + k] * H + h]);
+            dx[t * H + h] = orc_bf16_from_double(acc);
+        }
+}
+
+/* ------------------------------------------------------------------------ */
 /* Step 7: replica-gradient reduction.  [NCIJ] "The core idea": gradients of  */
 /* the duplicated experts go back to their home ranks; the "memory" panel:    */
 /* they sit in an fp32 reduce buffer, which the reduction pulls home and then */

@@ -42,6 +42,10 @@ MUTANTS = {
                            "dot += g * orc_bf16_to_double(out[(int64_t)slot_of[t * K] * H + h]);"),
     "bwd_dout_first_gate": ("orc_bf16_from_double((double)gates[n] * g);",
                             "orc_bf16_from_double((double)gates[t * K] * g);"),
+    "dispatch_bwd_drops_last_k": ("            for (int32_t k = 0; k < K; ++k)\n                acc += orc_bf16_to_double(d_buf",
+                                  "            for (int32_t k = 0; k + 1 < K; ++k)\n                acc += orc_bf16_to_double(d_buf"),
+    "dispatch_bwd_ignores_slot": ("acc += orc_bf16_to_double(d_buf[(int64_t)slot_of[t * K + k] * H + h]);",
+                                  "acc += orc_bf16_to_double(d_buf[(int64_t)(t * K + k) * H + h]);"),
     "reduce_skips_home": ("double acc = (double)home[(int64_t)e * G + i];\n            for (int32_t q",
                           "double acc = 0.0;\n            for (int32_t q"),
     "reduce_keeps_replicas": ("rep[(int64_t)q * G + i] = 0.0f;", "rep[(int64_t)q * G + i] = rep[(int64_t)q * G + i];"),

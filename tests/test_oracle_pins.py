@@ -647,3 +647,44 @@ def test_replica_reduce_random_exact_and_at():
     idx = np.array([0, 5, G - 1])
     at = oracle.replica_grad_reduce_at(w.E, pl, G, home[:, idx].copy(), rep[:pl.n_rep][:, idx].copy())
     np.testing.assert_array_equal(at, h2[:, idx])
+
+
+# ---------------------------------------------------------------------------
+# dispatch backward
+# ---------------------------------------------------------------------------
+
+def test_dispatch_bwd_exact_rational():
+    w, topk, gates, x, pl, slot_of, src_of_slot = tiny_forward()
+    d_buf = synth.normal_bf16(0, synth.TAG_DY, w.NK * w.H).reshape(w.NK, w.H)
+    dx = oracle.dispatch_bwd(w.K, w.H, d_buf, slot_of)
+    df = bf16_bits_to_f64(d_buf)
+    rng = np.random.default_rng(12)
+    for t in rng.choice(w.N, size=40, replace=False):
+        for h in rng.choice(w.H, size=8, replace=False):
+            exact = sum(Fraction(df[slot_of[t * w.K + k], h]) for k in range(w.K))
+            assert dx[t, h] == exact_bf16(exact)
+
+
+def test_dispatch_bwd_is_the_adjoint_of_dispatch():
+    w, topk, gates, x, pl, slot_of, src_of_slot = tiny_forward(seed=2)
+    # gathering back what dispatch scattered: every token's K rows are x[t]
+    buf = oracle.dispatch(w.K, w.H, x, slot_of)
+    dx = oracle.dispatch_bwd(w.K, w.H, buf, slot_of)
+    np.testing.assert_array_equal(dx, torch_bf16_bits(bf16_bits_to_f64(x).astype(np.float32) * w.K))
+    # <dispatch(u), D> = <u, dispatch_bwd(D)> up to the final rounding of dx
+    u = bf16_bits_to_f64(x)
+    D = synth.normal_bf16(1, synth.TAG_DY, w.NK * w.H).reshape(w.NK, w.H)
+    lhs = (bf16_bits_to_f64(oracle.dispatch(w.K, w.H, x, slot_of)) * bf16_bits_to_f64(D)).sum()
+    dxD = bf16_bits_to_f64(oracle.dispatch_bwd(w.K, w.H, D, slot_of))
+    assert abs((u * dxD).sum() - lhs) <= 2.0 ** -8 * (np.abs(u) * np.abs(dxD)).sum()
+
+
+def test_dispatch_bwd_one_hot_row():
+    w, topk, gates, x, pl, slot_of, src_of_slot = tiny_forward()
+    d_buf = np.zeros((w.NK, w.H), dtype=np.uint16)
+    n, h = 77, 5
+    d_buf[slot_of[n], h] = 0x4040          # 3.0
+    dx = bf16_bits_to_f64(oracle.dispatch_bwd(w.K, w.H, d_buf, slot_of))
+    want = np.zeros((w.N, w.H))
+    want[n // w.K, h] = 3.0
+    np.testing.assert_array_equal(dx, want)
