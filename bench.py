@@ -5,8 +5,9 @@ tokens per rank, K=8, H=2048 -- at maxvio 0, 0.5, 1, 2 and 4 (Zipf routing,
 exponent per level from tests/golden/sweep_alpha.json; level 0 balanced).
 Step i runs the whole path on level i mod 5, with every input resident in HBM:
 route_stats -> plan -> dispatch -> combine (identity expert, reading the
-dispatch buffer in place) -> combine_bwd -> replica_grad_reduce (expert
-weight-gradients of 2048 x 1408 fp32).
+dispatch buffer in place) -> combine_bwd -> dispatch_bwd (of combine_bwd's
+d_out: the identity expert's backward is the identity) -> replica_grad_reduce
+(expert weight-gradients of 2048 x 1408 fp32).
 
 Reported value: dispatch+combine GB/s = algorithmic bytes of the two calls
 divided by their HIP-event time inside the timed steps.  Algorithmic bytes
@@ -14,6 +15,7 @@ per call (what the call must move at least):
   dispatch    = N*H*2 (read x once) + NK*H*2 (write rows) + NK*4 (slot_of)
   combine     = NK*H*2 (read rows) + N*H*2 (write y) + NK*8 (slot_of, gates)
   combine_bwd = N*H*2 + 2*NK*H*2 + NK*12
+  dispatch_bwd = NK*H*2 (read rows) + N*H*2 (write dx) + NK*4 (slot_of)
   reduce      = sum over experts with replicas of (n_e + 2)*4G + n_rep*4G
 Also printed: per-call microseconds, plan latency per maxvio level, the
 roofline of the dominant kernel, and the CPU oracle timed on every level.
@@ -39,9 +41,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
-CALLS = ("route_stats", "plan", "dispatch", "combine", "combine_bwd", "replica_grad_reduce")
+CALLS = ("route_stats", "plan", "dispatch", "combine", "combine_bwd", "dispatch_bwd",
+         "replica_grad_reduce")
+MOVERS = ("dispatch", "combine", "combine_bwd", "dispatch_bwd")
 KERNEL_OF = {"dispatch": "dispatch_kernel", "combine": "combine_kernel",
-             "combine_bwd": "combine_bwd_kernel", "replica_grad_reduce": "replica_reduce_kernel"}
+             "combine_bwd": "combine_bwd_kernel", "dispatch_bwd": "dispatch_bwd_kernel",
+             "replica_grad_reduce": "replica_reduce_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sweep.json")
 WORKLOAD_NAME = {
     "sweep": "maxvio sweep R8 E64 S4096 K8 H2048, maxvio 0/0.5/1/2/4 cycled per step; "
@@ -59,6 +64,7 @@ def algorithmic_bytes(R, S, K, H, G=0, reps=None):
         "dispatch": N * H * 2 + NK * H * 2 + NK * 4,
         "combine": NK * H * 2 + N * H * 2 + NK * 8,
         "combine_bwd": N * H * 2 + 2 * NK * H * 2 + NK * 12,
+        "dispatch_bwd": NK * H * 2 + N * H * 2 + NK * 4,
     }
     if reps is not None:
         n_rep = int(sum(reps))
@@ -66,7 +72,7 @@ def algorithmic_bytes(R, S, K, H, G=0, reps=None):
     return d
 
 
-# Sources that define the dispatch, combine and combine_bwd kernels.
+# Sources that define the dispatch, combine, combine_bwd and dispatch_bwd kernels.
 MOVER_SOURCES = ("movers.hip", "moonep_internal.hpp")
 
 
@@ -206,6 +212,7 @@ def main():
     y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
     d_out = torch.empty((NK, H), dtype=torch.bfloat16, device=dev)
     d_g = torch.empty(NK, dtype=torch.float32, device=dev)
+    dx = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i, ev=None):
@@ -218,6 +225,7 @@ def main():
             lambda: mx.moonep_dispatch(s, x, b.slot_of, b.buf, stream),
             lambda: mx.moonep_combine(s, b.buf, gt, b.slot_of, y, stream),
             lambda: mx.moonep_combine_bwd(s, dy, b.buf, gt, b.slot_of, d_out, d_g, stream),
+            lambda: mx.moonep_dispatch_bwd(s, d_out, b.slot_of, dx, stream),
             lambda: mx.moonep_replica_grad_reduce(s, b.plan, G, home, rep, stream),
         )
         for c, fn in enumerate(calls):
@@ -277,7 +285,7 @@ def main():
                for lv in levels if per_level[lv]["plan"]}
     pv = list(plan_us.values())
     kern = {}
-    for name in ("dispatch", "combine", "combine_bwd", "replica_grad_reduce"):
+    for name in MOVERS + ("replica_grad_reduce",):
         if name == "replica_grad_reduce":
             per_lv = []
             for li, lv in enumerate(levels):
@@ -293,7 +301,7 @@ def main():
         kern[name] = {"us": us[name], "GBps": round(gbps, 1) if gbps else None,
                       "frac": round(gbps / HBM_PEAK_GBPS, 4) if gbps else None,
                       "bytes_per_launch": nbytes}
-    dominant = max(("dispatch", "combine", "combine_bwd"), key=lambda k: us[k])
+    dominant = max(MOVERS, key=lambda k: us[k])
     # HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary,
     # only while the kernel sources are those the counters were taken on.
     measured = {}

@@ -183,6 +183,16 @@ int moonep_combine_bwd(const moonep_shape *shape, const uint16_t *dy, const uint
                        float *d_gates, void *stream);
 
 /*
+ * Dispatch backward (the training backward of dispatch; [NCIJ "The core
+ * idea"]).  d_buf: bf16 [R*S*K, H], the gradient of the dispatch buffer rows.
+ * dx[t] = bf16(sum over k ascending of d_buf[slot_of[t*K+k]]), the sum taken in
+ * fp64 and rounded once (to nearest even).  dx: bf16 [R*S, H], must not overlap
+ * d_buf.  Out-of-range slots contribute nothing.
+ */
+int moonep_dispatch_bwd(const moonep_shape *shape, const uint16_t *d_buf, const int32_t *slot_of,
+                        uint16_t *dx, void *stream);
+
+/*
  * Replica-gradient reduction [NCIJ "The core idea": replica gradients return
  * to their home experts; explainer "memory" panel: they sit in an fp32 reduce
  * buffer that is pulled home and then zeroed for the next microbatch].

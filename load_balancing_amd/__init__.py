@@ -29,7 +29,8 @@ PLAN_HEADER = {"n_rep": 0, "n_spill": 1, "n_deficit": 2, "max_rep_rank": 3, "tma
 
 EXPORTS = ("moonep_check_shape", "moonep_workspace_bytes", "moonep_plan_layout_of",
            "moonep_plan_bytes", "moonep_route_stats", "moonep_plan", "moonep_dispatch",
-           "moonep_combine", "moonep_combine_bwd", "moonep_replica_grad_reduce",
+           "moonep_combine", "moonep_combine_bwd", "moonep_dispatch_bwd",
+           "moonep_replica_grad_reduce",
            "moonep_read_error")
 
 
@@ -88,6 +89,7 @@ def lib():
             "moonep_dispatch": (ctypes.c_int, [P, VP, VP, VP, VP]),
             "moonep_combine": (ctypes.c_int, [P, VP, VP, VP, VP, VP]),
             "moonep_combine_bwd": (ctypes.c_int, [P, VP, VP, VP, VP, VP, VP, VP]),
+            "moonep_dispatch_bwd": (ctypes.c_int, [P, VP, VP, VP, VP]),
             "moonep_replica_grad_reduce": (ctypes.c_int, [P, VP, I64, VP, VP, VP]),
             "moonep_read_error": (ctypes.c_int, [VP, SZ, ctypes.POINTER(ctypes.c_int32), VP]),
         }
@@ -212,6 +214,13 @@ def moonep_combine_bwd(shape, dy, expert_out, gates, slot_of, d_out, d_gates, st
         _dev(slot_of, "slot_of", shape.NK, ("int32",)),
         _dev(d_out, "d_out", shape.NK * shape.H, _BF16_OK),
         _dev(d_gates, "d_gates", shape.NK, ("float32",)), _stream(stream)), "moonep_combine_bwd")
+
+
+def moonep_dispatch_bwd(shape, d_buf, slot_of, dx, stream=None):
+    _check(lib().moonep_dispatch_bwd(
+        ctypes.byref(shape), _dev(d_buf, "d_buf", shape.NK * shape.H, _BF16_OK),
+        _dev(slot_of, "slot_of", shape.NK, ("int32",)),
+        _dev(dx, "dx", shape.N * shape.H, _BF16_OK), _stream(stream)), "moonep_dispatch_bwd")
 
 
 def moonep_replica_grad_reduce(shape, plan, G, home_grads, replica_grads, stream=None):

@@ -17,6 +17,8 @@ int launch_dispatch(const moonep_shape &s, const uint16_t *x, const int32_t *slo
                     hipStream_t st);
 int launch_combine(const moonep_shape &s, const uint16_t *out, const float *gates,
                    const int32_t *slot_of, uint16_t *y, hipStream_t st);
+int launch_dispatch_bwd(const moonep_shape &s, const uint16_t *d_buf, const int32_t *slot_of,
+                        uint16_t *dx, hipStream_t st);
 int launch_combine_bwd(const moonep_shape &s, const uint16_t *dy, const uint16_t *out,
                        const float *gates, const int32_t *slot_of, uint16_t *d_out, float *d_gates,
                        hipStream_t st);
@@ -200,6 +202,23 @@ int moonep_combine_bwd(const moonep_shape *shape, const uint16_t *dy, const uint
         return MOONEP_ERR_ALIAS;
     return launch_combine_bwd(*shape, dy, expert_out, gates, slot_of, d_out, d_gates,
                               (hipStream_t)stream);
+}
+
+int moonep_dispatch_bwd(const moonep_shape *shape, const uint16_t *d_buf, const int32_t *slot_of,
+                        uint16_t *dx, void *stream)
+{
+    int rc = shape_status(shape);
+    if (rc != MOONEP_OK)
+        return rc;
+    const int64_t nk = n_entries(shape), nt = n_tokens(shape);
+    if (!present(d_buf, nk) || !present(slot_of, nk) || !present(dx, nt))
+        return MOONEP_ERR_NULL_PTR;
+    if (!aligned(d_buf, 16) || !aligned(dx, 16) || !aligned(slot_of, 4))
+        return MOONEP_ERR_MISALIGNED;
+    const size_t row = (size_t)shape->H * 2;
+    if (overlap(d_buf, nk * row, dx, nt * row))
+        return MOONEP_ERR_ALIAS;
+    return launch_dispatch_bwd(*shape, d_buf, slot_of, dx, (hipStream_t)stream);
 }
 
 int moonep_replica_grad_reduce(const moonep_shape *shape, const int32_t *plan, int64_t G,

@@ -154,6 +154,26 @@ __device__ __forceinline__ uint32_t bf16_of_exact_product(float a, float b)
     return w & 0xFFFFu;
 }
 
+// bf16 bits of a double, rounded once to nearest even: round to fp32 with
+// round-to-odd (truncate toward zero, then set the last bit if anything was
+// dropped), then to bf16 with round-to-nearest-even.  Rounding to odd at 24
+// bits, at least two bits more than bf16's 8, makes the second rounding land
+// where a direct rounding of the double would (Boldo and Melquiond, "Emulation
+// of FMA and correctly rounded sums: proved algorithms using rounding to odd",
+// IEEE Trans. Computers 2008).
+__device__ __forceinline__ uint32_t bf16_of_double(double d)
+{
+    float f = (float)d;
+    if ((double)f != d && d == d) {
+        uint32_t u = __float_as_uint(f);
+        if (__builtin_fabs((double)f) > __builtin_fabs(d))
+            u -= 1;  // one fp32 step toward zero
+        u |= 1u;
+        f = __uint_as_float(u);
+    }
+    return pack_bf16(f, 0.0f) & 0xFFFFu;
+}
+
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 

@@ -41,7 +41,8 @@ inline int block_for(int32_t V)
 // dispatch 12, combine 8, combine_bwd 16 -- 3, 2 and 4 workgroups of 256
 // threads.  Uncapped, the same kernels ran 2-4% slower (combine 212 us
 // against 198 us on the 1.2 GB sweep step).
-constexpr int kDispatchWaves = 12, kCombineWaves = 8, kCombineBwdWaves = 16;
+constexpr int kDispatchWaves = 12, kCombineWaves = 8, kCombineBwdWaves = 16,
+              kDispatchBwdWaves = 12;
 
 // Dynamic LDS a workgroup of `threads` requests so that only
 // waves_per_cu / (threads / 64) of them fit in one CU's LDS; the kernels do not
@@ -234,6 +235,68 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const u32x4 *__restrict
     }
 }
 
+// dx[t] = bf16(sum_k d_buf[slot_of[t*K+k]]), summed in fp64 in ascending k
+// and rounded once; out-of-range slots contribute nothing.  Same grid and
+// hoisted loads as combine.
+template <int KT>
+__global__ __launch_bounds__(kBlock) void dispatch_bwd_kernel(const u32x4 *__restrict__ d_buf,
+                                                              const int32_t *__restrict__ slot_of,
+                                                              u32x4 *__restrict__ dx, int64_t N,
+                                                              int32_t V, int32_t nwb, int32_t cpb,
+                                                              int32_t K, uint32_t nrows)
+{
+    constexpr int kN = Slots<KT>::kN;
+    const uint64_t total = (uint64_t)N * (uint64_t)nwb;
+    for (uint64_t w = blockIdx.x; w < total; w += gridDim.x) {
+        uint64_t tok;
+        uint32_t wb;
+        if (nwb == 1) {
+            tok = w;
+            wb = 0;
+        } else if (w < 0xFFFFFFFFull) {
+            tok = (uint32_t)w / (uint32_t)nwb;
+            wb = (uint32_t)w - (uint32_t)tok * (uint32_t)nwb;
+        } else {
+            tok = w / (uint64_t)nwb;
+            wb = (uint32_t)(w - tok * (uint64_t)nwb);
+        }
+        const int32_t v_end = (int32_t)((wb + 1) * cpb * blockDim.x) < V
+                                  ? (int32_t)((wb + 1) * cpb * blockDim.x) : V;
+        for (int32_t v = (int32_t)(wb * cpb * blockDim.x + threadIdx.x); v < v_end;
+             v += (int32_t)blockDim.x) {
+            const int32_t *so = slot_of + (int64_t)tok * K;
+            double acc[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[j] = 0.0;
+            for (int32_t k0 = 0; k0 < K; k0 += kN) {
+                Slots<KT> sl;
+                sl.load(so, nullptr, K, k0, nrows, false);
+                u32x4 o[kN];
+#pragma unroll
+                for (int c = 0; c < kN; ++c)
+                    o[c] = load_nt(d_buf + (int64_t)(sl.s[c] != 0xFFFFFFFFu ? sl.s[c] : 0u) * V + v);
+#pragma unroll
+                for (int c = 0; c < kN; ++c) {
+                    const bool use = sl.s[c] != 0xFFFFFFFFu;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const double a0 = acc[2 * j] + (double)bf16_lo(o[c][j]);
+                        const double a1 = acc[2 * j + 1] + (double)bf16_hi(o[c][j]);
+                        acc[2 * j] = use ? a0 : acc[2 * j];
+                        acc[2 * j + 1] = use ? a1 : acc[2 * j + 1];
+                    }
+                }
+            }
+            u32x4 r;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                r[j] = bf16_of_double(acc[2 * j]) | (bf16_of_double(acc[2 * j + 1]) << 16);
+            store_nt(dx + (int64_t)tok * V + v, r);
+        }
+    }
+}
+
 // d_out[slot_of[n]] = bf16(g_n * dy[tok]) (exact product, one rounding);
 // d_gates[n] = <dy[tok], out[slot_of[n]]> in fp32: per-thread partial dots
 // over its columns, then a wave butterfly and a cross-wave sum in LDS.
@@ -341,6 +404,15 @@ void run_combine(dim3 g, dim3 b, hipStream_t st, const u32x4 *out, const float *
 }
 
 template <int KT>
+void run_dispatch_bwd(dim3 g, dim3 b, hipStream_t st, const u32x4 *d_buf, const int32_t *so,
+                      u32x4 *dx, int64_t N, int32_t V, int32_t nwb, int32_t cpb, int32_t K,
+                      uint32_t nrows)
+{
+    hipLaunchKernelGGL(dispatch_bwd_kernel<KT>, g, b, residency_lds(kDispatchBwdWaves, (int)b.x), st,
+                       d_buf, so, dx, N, V, nwb, cpb, K, nrows);
+}
+
+template <int KT>
 void run_combine_bwd(dim3 g, dim3 b, hipStream_t st, const u32x4 *dy, const u32x4 *out,
                      const float *gates, const int32_t *so, u32x4 *d_out, float *d_gates, int32_t V,
                      int32_t K, uint32_t nrows)
@@ -387,6 +459,25 @@ int launch_combine(const moonep_shape &s, const uint16_t *out, const float *gate
     const uint32_t grid = (uint32_t)(total < (1 << 24) ? total : (1 << 24));
     MOONEP_BY_K(s.K, run_combine, dim3(grid), dim3(bs), st, (const u32x4 *)out, gates, slot_of,
                 (u32x4 *)y, N, V, nwb, cpb, s.K, nrows);
+    return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
+}
+
+int launch_dispatch_bwd(const moonep_shape &s, const uint16_t *d_buf, const int32_t *slot_of,
+                        uint16_t *dx, hipStream_t st)
+{
+    const int64_t N = (int64_t)s.R * s.S;
+    if (N == 0)
+        return MOONEP_OK;
+    const int32_t V = s.H / 8;
+    const uint32_t nrows = (uint32_t)(N * s.K);
+    const int bs = block_for(V);
+    const int32_t ncb = (V + bs - 1) / bs;
+    const int32_t cpb = ncb < 4 ? ncb : 1;  // column blocks per workgroup, as combine
+    const int32_t nwb = (ncb + cpb - 1) / cpb;
+    const int64_t total = N * nwb;
+    const uint32_t grid = (uint32_t)(total < (1 << 24) ? total : (1 << 24));
+    MOONEP_BY_K(s.K, run_dispatch_bwd, dim3(grid), dim3(bs), st, (const u32x4 *)d_buf, slot_of,
+                (u32x4 *)dx, N, V, nwb, cpb, s.K, nrows);
     return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
 }
 

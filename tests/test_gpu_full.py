@@ -101,6 +101,24 @@ def test_sweep_level_full(level):
     du = ulp_diff(bits(y), o_y)
     assert du.max() <= 1
     print(f"[sweep {level}] n_rep={pl.n_rep} combine exact fraction={float((du == 0).mean()):.6f}")
+    del y, o_y
+    # backward in full: combine_bwd's d_out, the stand-in expert's backward,
+    # dispatch_bwd's dx (all bit-exact)
+    dy = synth.activations(w, 0, synth.TAG_DY)
+    d_out = torch.empty_like(out)
+    d_g = torch.empty((w.NK,), dtype=torch.float32, device="cuda")
+    mx.moonep_combine_bwd(s, bf16_dev(dy), out, to_dev(gates), b.slot_of, d_out, d_g)
+    del out
+    d_buf = stand_in_expert(d_topk, b.src_of_slot, to_dev(scale), d_out)
+    dx = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
+    mx.moonep_dispatch_bwd(s, d_buf, b.slot_of, dx)
+    o_dout, _ = oracle.combine_bwd(w.K, w.H, dy, o_out, gates, slot_of)
+    del o_out
+    np.testing.assert_array_equal(bits(d_out), o_dout)
+    o_dbuf = oracle.expert(w.H, o_dout, oracle.row_expert(topk, src_of_slot), scale)
+    del o_dout
+    np.testing.assert_array_equal(bits(d_buf), o_dbuf)
+    np.testing.assert_array_equal(bits(dx), oracle.dispatch_bwd(w.K, w.H, o_dbuf, slot_of))
 
 
 def test_dsv3_forward_sampled():
@@ -160,7 +178,21 @@ def test_dsv3_backward_sampled():
     f = lambda a: (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     l1 = np.abs(f(dy[toks]).repeat(w.K, 0) * f(out_rows)).sum(1)
     assert (np.abs(g - o_dg) <= 1e-5 * l1).all()
-    del out, d_out, d_dy
+    del out, d_dy
+
+    # dispatch backward through the stand-in expert's backward: every token
+    # of the sample, all K of its rows from the oracle
+    d_buf = stand_in_expert(d_topk, b.src_of_slot, to_dev(scale), d_out)
+    del d_out
+    dx = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
+    dx.view(torch.int16).fill_(-1)
+    mx.moonep_dispatch_bwd(s, d_buf, b.slot_of, dx)
+    torch.cuda.synchronize()
+    o_dbuf = oracle.expert(w.H, o_dout, topk[src_of_slot[rows]], scale)
+    np.testing.assert_array_equal(bits(d_buf[torch.from_numpy(rows).cuda()]), o_dbuf)
+    o_dx = oracle.dispatch_bwd(w.K, w.H, o_dbuf, np.arange(len(sub_ent), dtype=np.int32))
+    np.testing.assert_array_equal(bits(dx[torch.from_numpy(toks).cuda()]), o_dx)
+    del d_buf, dx
 
     # replica-gradient reduction, G = 7168 * 2048
     G = w.G

@@ -1,9 +1,11 @@
 """GPU parity at sizes the oracle covers element by element.
 
 Every case runs the whole path through the C-ABI (route_stats, plan,
-dispatch, stand-in expert, combine, combine_bwd, replica_grad_reduce) and
-compares every output with the CPU oracle:
-  counts, maxvio, plan, slot maps, dispatch buffer, d_out, replica grads: bit-exact;
+dispatch, stand-in expert, combine, combine_bwd, the stand-in expert's
+backward, dispatch_bwd, replica_grad_reduce) and compares every output with
+the CPU oracle:
+  counts, maxvio, plan, slot maps, dispatch buffer, d_out, dx, replica grads:
+  bit-exact;
   combine output: within 1 bf16 ulp (fp32 accumulation against the fp64 oracle);
   gate gradients: |gpu - oracle| <= 1e-5 * sum_h |dy_h * out_h|.
 """
@@ -44,6 +46,8 @@ def run_and_compare(w, seed, topk=None, gates=None, G=None):
     o_out = oracle.expert(w.H, o_buf, oracle.row_expert(topk, src_of_slot), scale)
     o_y = oracle.combine(w.K, w.H, o_out, gates, slot_of)
     o_dout, o_dg = oracle.combine_bwd(w.K, w.H, dy, o_out, gates, slot_of)
+    o_dbuf = oracle.expert(w.H, o_dout, oracle.row_expert(topk, src_of_slot), scale)
+    o_dx = oracle.dispatch_bwd(w.K, w.H, o_dbuf, slot_of)
     o_home, o_rep = oracle.replica_grad_reduce(w.E, pl, G, home, rep)
 
     # ---- GPU through the C-ABI ------------------------------------------
@@ -63,6 +67,10 @@ def run_and_compare(w, seed, topk=None, gates=None, G=None):
     d_out.view(torch.int16).fill_(-1)
     d_g = torch.full((w.NK,), float("nan"), dtype=torch.float32, device="cuda")
     mx.moonep_combine_bwd(s, d_dy, out, d_gates, b.slot_of, d_out, d_g)
+    d_buf = stand_in_expert(d_topk, b.src_of_slot, to_dev(scale), d_out)
+    dx = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
+    dx.view(torch.int16).fill_(-1)
+    mx.moonep_dispatch_bwd(s, d_buf, b.slot_of, dx)
     d_home = to_dev(home)
     d_rep = to_dev(rep)
     mx.moonep_replica_grad_reduce(s, b.plan, G, d_home, d_rep)
@@ -86,6 +94,8 @@ def run_and_compare(w, seed, topk=None, gates=None, G=None):
         l1 = np.abs(bf16_f64(dy)[np.arange(w.NK) // w.K] * bf16_f64(o_out)[slot_of]).sum(1)
         err = np.abs(g_gpu - o_dg.astype(np.float64))
         assert (err <= 1e-5 * l1 + 1e-30).all(), f"gate grad err {err.max()}"
+    np.testing.assert_array_equal(bits(d_buf), o_dbuf)
+    np.testing.assert_array_equal(bits(dx), o_dx)
     np.testing.assert_array_equal(d_home.cpu().numpy(), o_home)
     np.testing.assert_array_equal(d_rep.cpu().numpy(), o_rep)
     return {"exact_y": float((du == 0).mean()) if du.size else 1.0, "n_rep": pl.n_rep}
@@ -168,6 +178,15 @@ def test_bad_expert_id_sets_error_word_and_stays_in_bounds():
     # the other entries still form valid distinct slots
     rest = np.delete(so, [5, 77])
     assert (rest >= 0).all() and (rest < w.NK).all() and len(set(rest.tolist())) == rest.size
+    # dispatch_bwd skips the two unplaced entries: their tokens sum the other
+    # K-1 rows (the oracle sees them as a row of zeros appended to d_buf)
+    d_buf = synth.normal_bf16(3, synth.TAG_DY, w.NK * w.H).reshape(w.NK, w.H)
+    dx = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
+    mx.moonep_dispatch_bwd(s, bf16_dev(d_buf), b.slot_of, dx)
+    torch.cuda.synchronize()
+    padded = np.concatenate([d_buf, np.zeros((1, w.H), np.uint16)])
+    want = oracle.dispatch_bwd(w.K, w.H, padded, np.where(so < 0, w.NK, so).astype(np.int32))
+    np.testing.assert_array_equal(bits(dx), want)
 
 
 def test_repeat_is_bitwise_deterministic():
