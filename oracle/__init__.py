@@ -104,6 +104,10 @@ def lib():
         L.orc_replica_grad_reduce.argtypes = [i32, ctypes.POINTER(_CPlan), i64, p, p]
         L.orc_replica_grad_reduce_at.restype = None
         L.orc_replica_grad_reduce_at.argtypes = [i32, ctypes.POINTER(_CPlan), i64, p, p, i64, p]
+        L.orc_weight_slots.restype = None
+        L.orc_weight_slots.argtypes = [i32, i32, i32, ctypes.POINTER(_CPlan), p]
+        L.orc_prefetch_weights.restype = None
+        L.orc_prefetch_weights.argtypes = [i64, ctypes.POINTER(_CPlan), p, p, p]
         _lib = L
     return _lib
 
@@ -275,6 +279,26 @@ def replica_grad_reduce_at(E, pl: Plan, G, home_at, rep_at):
     c = _cplan_from(pl)
     lib().orc_replica_grad_reduce_at(E, ctypes.byref(c), G, _p(home_at), _p(rep_at), m, _p(out))
     return out
+
+
+def weight_slots(R, E, B, pl: Plan):
+    """wslot [E+R] int32: prefetch slot d*B+b of each replica, -1 for overflow and j >= n_rep."""
+    wslot = np.empty(E + R, dtype=np.int32)
+    c = _cplan_from(pl)
+    lib().orc_weight_slots(R, E, B, ctypes.byref(c), _p(wslot))
+    return wslot
+
+
+def prefetch_weights(pl: Plan, wslot, w_home, pool):
+    """Copy of pool [R*B, wbytes] uint8 with every slotted replica's expert row of w_home [E, wbytes]."""
+    w_home = _c(w_home, np.uint8)
+    wslot = _c(wslot, np.int32)
+    pool = np.array(pool, dtype=np.uint8, copy=True, order="C")
+    wbytes = w_home.shape[1]
+    assert pool.ndim == 2 and pool.shape[1] == wbytes
+    c = _cplan_from(pl)
+    lib().orc_prefetch_weights(wbytes, ctypes.byref(c), _p(wslot), _p(w_home), _p(pool))
+    return pool
 
 
 def row_expert(topk, src_of_slot):

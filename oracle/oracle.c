@@ -512,3 +512,45 @@ void orc_replica_grad_reduce_at(int32_t E, const orc_plan_t *p, int64_t G, const
         }
     (void)G;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Step 8: replica weight slots and prefetch.  [NCIJ] explainer, "memory"    */
+/* panel: every rank owns B prefetch slots, rows [E, E+B) of one contiguous  */
+/* weight tensor that follow the expert rows; training needs B = E/R,        */
+/* inference may use fewer (3-4); a rank needing more distinct remote        */
+/* experts than B reads the extra ones from their home rank ("overflow").    */
+/* "The core idea": the redundant experts are prefetched before expert       */
+/* compute.                                                                  */
+/*                                                                          */
+/* Slots: rank d's replicas, in plan order, take d's slots 0, 1, ..., B-1;   */
+/* wslot[j] = d*B + b for the b-th replica hosted on d when b < B, else -1   */
+/* (overflow).  Entries j >= n_rep are -1.  The plan itself is unchanged.    */
+/* ------------------------------------------------------------------------ */
+
+void orc_weight_slots(int32_t R, int32_t E, int32_t B, const orc_plan_t *p, int32_t *wslot)
+{
+    for (int32_t j = 0; j < E + R; ++j)
+        wslot[j] = -1;
+    for (int32_t d = 0; d < R; ++d) {
+        int32_t b = 0;  /* replicas of rank d seen so far, in plan order */
+        for (int32_t j = 0; j < p->n_rep; ++j) {
+            if (p->rep_host[j] != d)
+                continue;
+            if (b < B)
+                wslot[j] = d * B + b;
+            ++b;
+        }
+    }
+}
+
+/* Prefetch: the weight bytes of a replica's expert go to its slot.
+ *   pool[wslot[j]] = w_home[rep_expert[j]]   (wbytes bytes, a bit copy)
+ * for every j < n_rep with wslot[j] >= 0; other pool rows are untouched. */
+void orc_prefetch_weights(int64_t wbytes, const orc_plan_t *p, const int32_t *wslot,
+                          const uint8_t *w_home, uint8_t *pool)
+{
+    for (int32_t j = 0; j < p->n_rep; ++j)
+        if (wslot[j] >= 0)
+            memcpy(pool + (int64_t)wslot[j] * wbytes, w_home + (int64_t)p->rep_expert[j] * wbytes,
+                   (size_t)wbytes);
+}

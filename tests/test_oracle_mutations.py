@@ -46,6 +46,11 @@ MUTANTS = {
                                   "            for (int32_t k = 0; k + 1 < K; ++k)\n                acc += orc_bf16_to_double(d_buf"),
     "dispatch_bwd_ignores_slot": ("acc += orc_bf16_to_double(d_buf[(int64_t)slot_of[t * K + k] * H + h]);",
                                   "acc += orc_bf16_to_double(d_buf[(int64_t)(t * K + k) * H + h]);"),
+    "weight_slot_ignores_rank_base": ("wslot[j] = d * B + b;", "wslot[j] = b;"),
+    "weight_slot_cap_off_by_one": ("            if (b < B)\n                wslot[j]", "            if (b <= B)\n                wslot[j]"),
+    "weight_slot_counts_other_ranks": ("            if (p->rep_host[j] != d)\n                continue;",
+                                       "            if (p->rep_host[j] != d && ++b)\n                continue;"),
+    "prefetch_wrong_source": ("w_home + (int64_t)p->rep_expert[j] * wbytes", "w_home + (int64_t)p->rep_host[j] * wbytes"),
     "reduce_skips_home": ("double acc = (double)home[(int64_t)e * G + i];\n            for (int32_t q",
                           "double acc = 0.0;\n            for (int32_t q"),
     "reduce_keeps_replicas": ("rep[(int64_t)q * G + i] = 0.0f;", "rep[(int64_t)q * G + i] = rep[(int64_t)q * G + i];"),

@@ -275,6 +275,10 @@ def test_hand_examples(ex):
     slot_of, src_of_slot = oracle.slots(R, E, S, K, topk, pl)
     assert slot_of.tolist() == ex["slot_of"]
     assert (src_of_slot[slot_of] == np.arange(len(topk))).all()
+    for B, want in ex["weight_slots"].items():
+        ws = oracle.weight_slots(R, E, int(B), pl)
+        assert ws[:pl.n_rep].tolist() == want
+        assert (ws[pl.n_rep:] == -1).all()
 
 
 def test_counts_match_bincount_and_sum():
@@ -688,3 +692,93 @@ def test_dispatch_bwd_one_hot_row():
     want = np.zeros((w.N, w.H))
     want[n // w.K, h] = 3.0
     np.testing.assert_array_equal(dx, want)
+
+
+# ---------------------------------------------------------------------------
+# Replica weight slots and prefetch (explainer "memory" panel)
+# ---------------------------------------------------------------------------
+
+def check_weight_slots(R, E, B, pl, ws):
+    """Invariants the panel fixes: a rank's slots are its own B rows, used by
+    its replicas in plan order; overflow only past B replicas."""
+    assert ws.shape == (E + R,) and (ws[pl.n_rep:] == -1).all()
+    for d in range(R):
+        mine = [j for j in range(pl.n_rep) if pl.rep_host[j] == d]
+        got = [int(ws[j]) for j in mine]
+        want = [d * B + b if b < B else -1 for b in range(len(mine))]
+        assert got == want, (d, got, want)
+    used = ws[ws >= 0]
+    assert len(set(used.tolist())) == used.size
+    assert ((used >= 0) & (used < R * B)).all()
+    assert (ws[:pl.n_rep] >= 0).sum() == sum(min(B, int(c)) for c in pl.rank_rep_cnt)
+
+
+def test_weight_slots_random_tiny():
+    rng = np.random.default_rng(11)
+    seen_overflow = 0
+    for trial in range(200):
+        R = int(rng.integers(1, 6))
+        L = int(rng.integers(1, 4))
+        E = R * L
+        K = int(rng.integers(1, E + 1))
+        S = int(rng.integers(1, 9))
+        w = synth.Workload("t", R, E, S, K, 8, "zipf", alpha=float(rng.uniform(0, 2.5)))
+        topk, _ = synth.routing(w, trial)
+        T, _ = oracle.route_stats(R, E, S, K, topk)
+        pl = oracle.plan(R, E, S, K, T)
+        for B in (0, 1, 2, L, pl.max_rep_rank):
+            ws = oracle.weight_slots(R, E, B, pl)
+            check_weight_slots(R, E, B, pl, ws)
+            if B >= pl.max_rep_rank:
+                assert (ws[:pl.n_rep] >= 0).all()
+            seen_overflow += int((ws[:pl.n_rep] < 0).any())
+    assert seen_overflow > 0
+
+
+def test_weight_slots_adversarial_closed_form():
+    # 15 replicas, replica j hosted alone on rank j + 1, so every rank d >= 1
+    # fills slot d*B with expert (d - 1) div 2 (expert 7 on rank 15)
+    w = synth.WORKLOADS["adversarial"]
+    topk, _ = synth.routing(w, 0)
+    T, _ = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
+    for B in (1, 4, w.E // w.R):
+        ws = oracle.weight_slots(w.R, w.E, B, pl)
+        assert ws[:15].tolist() == [(j + 1) * B for j in range(15)]
+        assert (ws[15:] == -1).all()
+    wbytes = 48
+    rng = np.random.default_rng(5)
+    w_home = rng.integers(0, 256, (w.E, wbytes), dtype=np.uint8)
+    B = 2
+    ws = oracle.weight_slots(w.R, w.E, B, pl)
+    pool = oracle.prefetch_weights(pl, ws, w_home, np.full((w.R * B, wbytes), 0xA5, np.uint8))
+    assert (pool[0] == 0xA5).all()                  # rank 0 hosts no replica
+    for d in range(1, w.R):
+        e = 7 if d == 15 else (d - 1) // 2
+        assert (pool[d * B] == w_home[e]).all()
+    assert (pool[1::B] == 0xA5).all()               # second slots stay unused
+
+
+def test_prefetch_is_a_gather_of_expert_rows():
+    rng = np.random.default_rng(3)
+    for trial in range(40):
+        R = int(rng.integers(1, 5))
+        L = int(rng.integers(1, 4))
+        E = R * L
+        K = int(rng.integers(1, E + 1))
+        S = int(rng.integers(1, 9))
+        w = synth.Workload("t", R, E, S, K, 8, "zipf", alpha=float(rng.uniform(0.5, 2.5)))
+        topk, _ = synth.routing(w, 100 + trial)
+        T, _ = oracle.route_stats(R, E, S, K, topk)
+        pl = oracle.plan(R, E, S, K, T)
+        B = int(rng.integers(0, L + 2))
+        ws = oracle.weight_slots(R, E, B, pl)
+        wbytes = 16 * int(rng.integers(1, 5))
+        w_home = rng.integers(0, 256, (E, wbytes), dtype=np.uint8)
+        before = rng.integers(0, 256, (R * B, wbytes), dtype=np.uint8)
+        pool = oracle.prefetch_weights(pl, ws, w_home, before)
+        # numpy restatement: slotted rows gather their expert, the rest stay
+        want = before.copy()
+        js = np.nonzero(ws[:pl.n_rep] >= 0)[0]
+        want[ws[js]] = w_home[pl.rep_expert[js]]
+        np.testing.assert_array_equal(pool, want)
