@@ -4,8 +4,9 @@ Workload: the maxvio sweep shape -- R=8 logical ranks, E=64 experts, S=4096
 tokens per rank, K=8, H=2048 -- at maxvio 0, 0.5, 1, 2 and 4 (Zipf routing,
 exponent per level from tests/golden/sweep_alpha.json; level 0 balanced).
 Step i runs the whole path on level i mod 5, with every input resident in HBM:
-route_stats -> plan -> dispatch -> combine (identity expert, reading the
-dispatch buffer in place) -> combine_bwd -> dispatch_bwd (of combine_bwd's
+route_stats -> plan -> weight_slots + prefetch_weights (training B = E/R
+slots per rank; expert weights gate+up+down = 3 x 2048 x 1408 bf16) ->
+dispatch -> combine (identity expert, reading the dispatch buffer in place) -> combine_bwd -> dispatch_bwd (of combine_bwd's
 d_out: the identity expert's backward is the identity) -> replica_grad_reduce
 (expert weight-gradients of 2048 x 1408 fp32).
 
@@ -16,6 +17,7 @@ per call (what the call must move at least):
   combine     = NK*H*2 (read rows) + N*H*2 (write y) + NK*8 (slot_of, gates)
   combine_bwd = N*H*2 + 2*NK*H*2 + NK*12
   dispatch_bwd = NK*H*2 (read rows) + N*H*2 (write dx) + NK*4 (slot_of)
+  prefetch    = 2 * (replicas given a slot) * (expert weight bytes)
   reduce      = sum over experts with replicas of (n_e + 2)*4G + n_rep*4G
 Also printed: per-call microseconds, plan latency per maxvio level, the
 roofline of the dominant kernel, and the CPU oracle timed on every level.
@@ -41,20 +43,22 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
-CALLS = ("route_stats", "plan", "dispatch", "combine", "combine_bwd", "dispatch_bwd",
-         "replica_grad_reduce")
+CALLS = ("route_stats", "plan", "weight_slots", "prefetch", "dispatch", "combine", "combine_bwd",
+         "dispatch_bwd", "replica_grad_reduce")
 MOVERS = ("dispatch", "combine", "combine_bwd", "dispatch_bwd")
 KERNEL_OF = {"dispatch": "dispatch_kernel", "combine": "combine_kernel",
              "combine_bwd": "combine_bwd_kernel", "dispatch_bwd": "dispatch_bwd_kernel",
-             "replica_grad_reduce": "replica_reduce_kernel"}
+             "replica_grad_reduce": "replica_reduce_kernel", "prefetch": "prefetch_kernel"}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_sweep.json")
 WORKLOAD_NAME = {
     "sweep": "maxvio sweep R8 E64 S4096 K8 H2048, maxvio 0/0.5/1/2/4 cycled per step; "
-             "backward weight-grads 2048x1408 fp32",
-    "dsv3": "DeepSeek-V3-like R32 E256 S4096 K8 H7168, Zipf 1.2; backward weight-grads "
-            "7168x2048 fp32",
+             "expert weights 3x2048x1408 bf16 with E/R prefetch slots per rank; backward "
+             "weight-grads 2048x1408 fp32",
+    "dsv3": "DeepSeek-V3-like R32 E256 S4096 K8 H7168, Zipf 1.2; expert weights 3x7168x2048 bf16 "
+            "with E/R prefetch slots per rank; backward weight-grads 7168x2048 fp32",
     "adversarial": "adversarial R16 E128 S8192 K8 H4096, every token to experts 0..7, gates 1/8; "
-                   "backward weight-grads 4096x2048 fp32",
+                   "expert weights 3x4096x2048 bf16 with E/R prefetch slots per rank; backward "
+                   "weight-grads 4096x2048 fp32",
 }
 
 
@@ -208,6 +212,20 @@ def main():
         for j in range(cap):
             rep[j].copy_(pat_r[j % 8])
         del pat_h, pat_r
+    # expert weights (gate, up, down: 3 x H x H' bf16 = 6G bytes) and the
+    # training-sized prefetch pool of B = E/R slots per rank
+    B_slots = E // R
+    wbytes = 6 * G
+    if E * wbytes <= (1 << 31):
+        w_home = up(synth.expert_weights(E, wbytes, args.seed))
+    else:
+        pat = up(synth.expert_weights(8, wbytes, args.seed))
+        w_home = torch.empty((E, wbytes), dtype=torch.uint8, device=dev)
+        for e in range(E):
+            w_home[e].copy_(pat[e % 8])
+        del pat
+    pool = torch.empty((R * B_slots, wbytes), dtype=torch.uint8, device=dev)
+    wslot = torch.empty(E + R, dtype=torch.int32, device=dev)
     b = mx.allocate(s, dev)
     y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
     d_out = torch.empty((NK, H), dtype=torch.bfloat16, device=dev)
@@ -222,6 +240,9 @@ def main():
             lambda: mx.moonep_route_stats(s, tk, b.expert_counts, b.maxvio, b.workspace, stream),
             lambda: mx.moonep_plan(s, tk, b.expert_counts, b.workspace, b.plan, b.slot_of,
                                    b.src_of_slot, stream),
+            lambda: mx.moonep_weight_slots(s, b.plan, B_slots, wslot, stream),
+            lambda: mx.moonep_prefetch_weights(s, b.plan, wslot, B_slots, wbytes, w_home, pool,
+                                               stream),
             lambda: mx.moonep_dispatch(s, x, b.slot_of, b.buf, stream),
             lambda: mx.moonep_combine(s, b.buf, gt, b.slot_of, y, stream),
             lambda: mx.moonep_combine_bwd(s, dy, b.buf, gt, b.slot_of, d_out, d_g, stream),
@@ -235,13 +256,15 @@ def main():
         if ev is not None:
             ev[len(calls)].record(stream)
 
-    # replica counts per level (for the reduce's algorithmic bytes)
-    reps_per_level = []
+    # replica counts per level (for the reduce's algorithmic bytes) and the
+    # replicas given a prefetch slot (for the prefetch's)
+    reps_per_level, pref_per_level = [], []
     for lv in range(len(levels)):
         step(lv)
         torch.cuda.synchronize()
         f = b.plan_fields()
         reps_per_level.append([int(c) for c in f["rep_cnt"]])
+        pref_per_level.append(int((wslot >= 0).sum().item()))
         assert mx.moonep_read_error(b.workspace) == 0
 
     if not args.no_copy_probe:
@@ -285,12 +308,13 @@ def main():
                for lv in levels if per_level[lv]["plan"]}
     pv = list(plan_us.values())
     kern = {}
-    for name in MOVERS + ("replica_grad_reduce",):
-        if name == "replica_grad_reduce":
+    for name in MOVERS + ("replica_grad_reduce", "prefetch"):
+        if name in ("replica_grad_reduce", "prefetch"):
             per_lv = []
             for li, lv in enumerate(levels):
                 if per_level[lv][name]:
-                    bb = algorithmic_bytes(R, S, K, H, G, reps_per_level[li])[name]
+                    bb = (algorithmic_bytes(R, S, K, H, G, reps_per_level[li])[name]
+                          if name == "replica_grad_reduce" else 2 * pref_per_level[li] * wbytes)
                     per_lv.append(bb / (1e-3 * mean(per_level[lv][name])) / 1e9 if bb else None)
             vals = [v for v in per_lv if v]
             gbps = mean(vals) if vals else None
@@ -333,12 +357,18 @@ def main():
                                                             mean(per_call["combine"]) +
                                                             mean(per_call["route_stats"]) +
                                                             mean(per_call["plan"]))) / 1e9, 1),
-        "tokens_per_s_forward": round(N / (1e-3 * sum(mean(per_call[c]) for c in CALLS[:4])), 0),
+        "tokens_per_s_forward": round(N / (1e-3 * sum(mean(per_call[c]) for c in
+                                                       ("route_stats", "plan", "dispatch",
+                                                        "combine"))), 0),
         "plan_us_vs_maxvio": plan_us,
         "plan_spread": round((max(pv) - min(pv)) / min(pv), 4) if pv else None,
         "breakdown_us": us,
         "kernels": kern,
         "replicas_per_level": {lv: int(sum(r)) for lv, r in zip(levels, reps_per_level)},
+        "prefetch": {"B": B_slots, "weight_bytes_per_expert": wbytes,
+                     "prefetched_per_level": dict(zip(levels, pref_per_level)),
+                     "overflow_per_level": {lv: int(sum(r)) - p for lv, r, p in
+                                            zip(levels, reps_per_level, pref_per_level)}},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

@@ -206,6 +206,36 @@ int moonep_replica_grad_reduce(const moonep_shape *shape, const int32_t *plan, i
                                float *home_grads, float *replica_grads, void *stream);
 
 /*
+ * Replica weight slots [NCIJ "The core idea": redundant experts are
+ * prefetched before expert compute; explainer "memory" panel: each rank owns B
+ * prefetch slots, the rows that follow the expert rows of its weight tensor;
+ * training needs B = E/R, inference may use fewer (3-4 suggested), and a rank
+ * that hosts more than B replicas reads the extra ones from their home rank].
+ * Writes wslot: int32 [E + R], for replica j < n_rep of `plan` hosted on rank
+ * d as its b-th in plan order: wslot[j] = d*B + b when b < B, else -1
+ * (overflow: that replica's weights are read at the home expert's row).
+ * Entries j >= n_rep are -1.  The plan is not changed.  B >= 0 and
+ * R*B < 2^31, else MOONEP_ERR_ARG.
+ */
+int moonep_weight_slots(const moonep_shape *shape, const int32_t *plan, int32_t B, int32_t *wslot,
+                        void *stream);
+
+/*
+ * Replica weight prefetch [same passages].  w_home: [E, wbytes] bytes, row e =
+ * every weight of expert e (e.g. its gate, up and down projections, in any
+ * layout the caller chooses); pool: [R*B, wbytes] bytes, row d*B + b = slot b
+ * of rank d.  For every j < n_rep with 0 <= wslot[j] < R*B:
+ *   pool[wslot[j]] = w_home[rep_expert[j]]  (a bit copy).
+ * Other pool rows are not touched.  wbytes % 16 == 0 (MOONEP_ERR_ARG);
+ * w_home and pool 16-byte aligned; they must not overlap.  wslot normally
+ * comes from moonep_weight_slots with the same B; slots that two replicas
+ * share would race.
+ */
+int moonep_prefetch_weights(const moonep_shape *shape, const int32_t *plan, const int32_t *wslot,
+                            int32_t B, int64_t wbytes, const void *w_home, void *pool,
+                            void *stream);
+
+/*
  * Reads the sticky device error word of a workspace into *host_code, then
  * clears it.  Synchronises `stream`.  The only call that waits for the device.
  */

@@ -30,7 +30,7 @@ PLAN_HEADER = {"n_rep": 0, "n_spill": 1, "n_deficit": 2, "max_rep_rank": 3, "tma
 EXPORTS = ("moonep_check_shape", "moonep_workspace_bytes", "moonep_plan_layout_of",
            "moonep_plan_bytes", "moonep_route_stats", "moonep_plan", "moonep_dispatch",
            "moonep_combine", "moonep_combine_bwd", "moonep_dispatch_bwd",
-           "moonep_replica_grad_reduce",
+           "moonep_replica_grad_reduce", "moonep_weight_slots", "moonep_prefetch_weights",
            "moonep_read_error")
 
 
@@ -91,6 +91,8 @@ def lib():
             "moonep_combine_bwd": (ctypes.c_int, [P, VP, VP, VP, VP, VP, VP, VP]),
             "moonep_dispatch_bwd": (ctypes.c_int, [P, VP, VP, VP, VP]),
             "moonep_replica_grad_reduce": (ctypes.c_int, [P, VP, I64, VP, VP, VP]),
+            "moonep_weight_slots": (ctypes.c_int, [P, VP, ctypes.c_int32, VP, VP]),
+            "moonep_prefetch_weights": (ctypes.c_int, [P, VP, VP, ctypes.c_int32, I64, VP, VP, VP]),
             "moonep_read_error": (ctypes.c_int, [VP, SZ, ctypes.POINTER(ctypes.c_int32), VP]),
         }
         for name, (res, args) in sig.items():
@@ -229,6 +231,38 @@ def moonep_replica_grad_reduce(shape, plan, G, home_grads, replica_grads, stream
         int(G), _dev(home_grads, "home_grads", shape.E * G, ("float32",)),
         _dev(replica_grads, "replica_grads", (shape.E + shape.R) * G, ("float32",)),
         _stream(stream)), "moonep_replica_grad_reduce")
+
+
+def moonep_weight_slots(shape, plan, B, wslot, stream=None):
+    _check(lib().moonep_weight_slots(
+        ctypes.byref(shape), _dev(plan, "plan", moonep_plan_bytes(shape) // 4, ("int32",)),
+        int(B), _dev(wslot, "wslot", shape.E + shape.R, ("int32",)), _stream(stream)),
+        "moonep_weight_slots")
+
+
+def _dev_bytes(t, what, nbytes):
+    """Device pointer of a contiguous tensor of any dtype holding exactly nbytes."""
+    if t is None:
+        if nbytes == 0:
+            return None
+        raise MoonepError(what, -2)
+    if not t.is_cuda:
+        raise ValueError(f"{what}: tensor must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: tensor must be contiguous")
+    if _nbytes(t) != nbytes:
+        raise ValueError(f"{what}: has {_nbytes(t)} bytes, needs {nbytes}")
+    return t.data_ptr()
+
+
+def moonep_prefetch_weights(shape, plan, wslot, B, wbytes, w_home, pool, stream=None):
+    """pool [R*B, wbytes] gets each slotted replica's row of w_home [E, wbytes]."""
+    _check(lib().moonep_prefetch_weights(
+        ctypes.byref(shape), _dev(plan, "plan", moonep_plan_bytes(shape) // 4, ("int32",)),
+        _dev(wslot, "wslot", shape.E + shape.R, ("int32",)), int(B), int(wbytes),
+        _dev_bytes(w_home, "w_home", shape.E * wbytes),
+        _dev_bytes(pool, "pool", shape.R * B * wbytes), _stream(stream)),
+        "moonep_prefetch_weights")
 
 
 def moonep_read_error(workspace, stream=None) -> int:

@@ -24,6 +24,10 @@ int launch_combine_bwd(const moonep_shape &s, const uint16_t *dy, const uint16_t
                        hipStream_t st);
 int launch_replica_reduce(const moonep_shape &s, const int32_t *plan, int64_t G, float *home,
                           float *rep, int grid, hipStream_t st);
+int launch_weight_slots(const moonep_shape &s, const int32_t *plan, int32_t B, int32_t *wslot,
+                        hipStream_t st);
+int launch_prefetch(const moonep_shape &s, const int32_t *plan, const int32_t *wslot, int32_t B,
+                    int64_t wbytes, const void *w_home, void *pool, int grid, hipStream_t st);
 }  // namespace moonep
 
 using namespace moonep;
@@ -243,6 +247,44 @@ int moonep_replica_grad_reduce(const moonep_shape *shape, const int32_t *plan, i
         return MOONEP_ERR_HIP;
     return launch_replica_reduce(*shape, plan, G, home_grads, replica_grads, cus * 4,
                                  (hipStream_t)stream);
+}
+
+int moonep_weight_slots(const moonep_shape *shape, const int32_t *plan, int32_t B, int32_t *wslot,
+                        void *stream)
+{
+    int rc = shape_status(shape);
+    if (rc != MOONEP_OK)
+        return rc;
+    if (B < 0 || (int64_t)shape->R * B >= ((int64_t)1 << 31))
+        return MOONEP_ERR_ARG;
+    if (!plan || !wslot)
+        return MOONEP_ERR_NULL_PTR;
+    if (!aligned(plan, 4) || !aligned(wslot, 4))
+        return MOONEP_ERR_MISALIGNED;
+    return launch_weight_slots(*shape, plan, B, wslot, (hipStream_t)stream);
+}
+
+int moonep_prefetch_weights(const moonep_shape *shape, const int32_t *plan, const int32_t *wslot,
+                            int32_t B, int64_t wbytes, const void *w_home, void *pool, void *stream)
+{
+    int rc = shape_status(shape);
+    if (rc != MOONEP_OK)
+        return rc;
+    if (B < 0 || (int64_t)shape->R * B >= ((int64_t)1 << 31) || wbytes < 0 || wbytes % 16 != 0)
+        return MOONEP_ERR_ARG;
+    const int64_t pool_rows = (int64_t)shape->R * B;
+    if (!plan || !wslot || !present(w_home, wbytes) || !present(pool, pool_rows * wbytes))
+        return MOONEP_ERR_NULL_PTR;
+    if (!aligned(plan, 4) || !aligned(wslot, 4) || !aligned(w_home, 16) || !aligned(pool, 16))
+        return MOONEP_ERR_MISALIGNED;
+    if (overlap(w_home, (size_t)shape->E * (size_t)wbytes, pool, (size_t)pool_rows * (size_t)wbytes))
+        return MOONEP_ERR_ALIAS;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return MOONEP_ERR_HIP;
+    return launch_prefetch(*shape, plan, wslot, B, wbytes, w_home, pool, cus * 4,
+                           (hipStream_t)stream);
 }
 
 int moonep_read_error(void *workspace, size_t workspace_bytes, int32_t *host_code, void *stream)

@@ -27,6 +27,7 @@ _LIB = os.path.join(_HERE, "libsynth.so")
 
 # Stream tags (xor-ed into the per-seed key).
 TAG_PERM, TAG_ROUTE, TAG_LOGIT, TAG_X, TAG_DY, TAG_GRAD_REP, TAG_GRAD_HOME = 1, 2, 3, 4, 5, 6, 7
+TAG_WEIGHT = 8  # expert weights (bf16 N(0,1)), for the prefetch
 
 
 def build(verbose: bool = False) -> str:
@@ -197,7 +198,8 @@ class Workload:
 
 # Expert FFN width for the 64-expert, 2048-hidden sweep shape is not stated by
 # the workload; 1408 is the published width of a 64-expert MoE with hidden 2048
-# and serves only to size the replica-gradient tensors of the backward leg.
+# and serves only to size the expert weights (gate, up and down: 3 x 2048 x
+# 1408 bf16, for the prefetch) and their gradients (the backward reduce).
 SWEEP_FFN = 1408
 # The DeepSeek-V3-like expert weight-gradient: 7168 x 2048.
 DSV3_G = 7168 * 2048
@@ -248,6 +250,13 @@ def routing(w: Workload, seed: int) -> tuple[np.ndarray, np.ndarray]:
     else:
         gates = fill_f32(w.N * w.K, 1.0 / w.K)
     return topk, gates
+
+
+def expert_weights(E: int, wbytes: int, seed: int) -> np.ndarray:
+    """[E, wbytes] uint8: every expert's weights as bf16 bits of N(0,1), one
+    stream over all experts (a row is one expert's gate, up and down)."""
+    assert wbytes % 2 == 0
+    return normal_bf16(seed, TAG_WEIGHT, E * (wbytes // 2)).view(np.uint8).reshape(E, wbytes)
 
 
 def activations(w: Workload, seed: int, tag: int = TAG_X) -> np.ndarray:

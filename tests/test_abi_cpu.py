@@ -87,6 +87,23 @@ def test_host_errors_before_any_launch(L):
                                         None) == -7
     assert L.moonep_replica_grad_reduce(B(s), vp(fake), ctypes.c_int64(64), vp(fake),
                                         vp(fake + 64), None) == -6
+    # dispatch backward: null, misaligned, overlapping dx and d_buf
+    assert L.moonep_dispatch_bwd(B(s), None, vp(fake), vp(fake * 8), None) == -2
+    assert L.moonep_dispatch_bwd(B(s), vp(fake), vp(fake * 8), vp(fake * 16 + 8), None) == -3
+    assert L.moonep_dispatch_bwd(B(s), vp(fake), vp(fake * 8), vp(fake + 4096), None) == -6
+    # weight slots: negative B, null output
+    assert L.moonep_weight_slots(B(s), vp(fake), -1, vp(fake * 2), None) == -7
+    assert L.moonep_weight_slots(B(s), vp(fake), 2, None, None) == -2
+    # prefetch: wbytes not whole 16-byte vectors, misaligned pool, overlap
+    i64 = ctypes.c_int64
+    assert L.moonep_prefetch_weights(B(s), vp(fake), vp(fake * 2), 2, i64(24), vp(fake * 4),
+                                     vp(fake * 8), None) == -7
+    assert L.moonep_prefetch_weights(B(s), vp(fake), vp(fake * 2), 2, i64(32), vp(fake * 4),
+                                     vp(fake * 8 + 4), None) == -3
+    assert L.moonep_prefetch_weights(B(s), vp(fake), vp(fake * 2), 2, i64(32), vp(fake * 4),
+                                     vp(fake * 4 + 256), None) == -6
+    assert L.moonep_prefetch_weights(B(s), vp(fake), vp(fake * 2), 2, i64(32), None,
+                                     vp(fake * 8), None) == -2
     # invalid shape is reported first
     bad = mx.Shape(3, 16, 128, 2, 64)
     assert L.moonep_dispatch(B(bad), vp(fake), vp(fake), vp(fake * 4), None) == -1
