@@ -104,6 +104,9 @@ def lib():
         L.orc_replica_grad_reduce.argtypes = [i32, ctypes.POINTER(_CPlan), i64, p, p]
         L.orc_replica_grad_reduce_at.restype = None
         L.orc_replica_grad_reduce_at.argtypes = [i32, ctypes.POINTER(_CPlan), i64, p, p, i64, p]
+        L.orc_expert_gemm_rows.restype = None
+        L.orc_expert_gemm_rows.argtypes = [i32, i32, i32, i32, ctypes.POINTER(_CPlan), p, i32, i32,
+                                           p, p, p, i64, i64, i64, p, p]
         L.orc_weight_slots.restype = None
         L.orc_weight_slots.argtypes = [i32, i32, i32, ctypes.POINTER(_CPlan), p]
         L.orc_prefetch_weights.restype = None
@@ -299,6 +302,23 @@ def prefetch_weights(pl: Plan, wslot, w_home, pool):
     c = _cplan_from(pl)
     lib().orc_prefetch_weights(wbytes, ctypes.byref(c), _p(wslot), _p(w_home), _p(pool))
     return pool
+
+
+def expert_gemm(R, E, S, K, pl: Plan, wslot, in_dim, out_dim, x, w_home, pool, w_stride,
+                w_offset=0, rows=None):
+    """y [len(rows), out_dim] bf16 bits: one projection of the listed buffer rows
+    (all R*S*K rows if rows is None) by their segment's weight matrix."""
+    x = _c(x, np.uint16)
+    w_home = _c(w_home, np.uint16)
+    pool = _c(pool, np.uint16) if pool is not None and np.size(pool) else np.zeros(1, np.uint16)
+    wslot = _c(wslot, np.int32)
+    rows = np.arange(R * S * K, dtype=np.int64) if rows is None else _c(rows, np.int64)
+    y = np.empty((rows.size, out_dim), dtype=np.uint16)
+    c = _cplan_from(pl)
+    lib().orc_expert_gemm_rows(R, E, S, K, ctypes.byref(c), _p(wslot), in_dim, out_dim, _p(x),
+                               _p(w_home), _p(pool), w_stride, w_offset, rows.size, _p(rows),
+                               _p(y))
+    return y
 
 
 def row_expert(topk, src_of_slot):

@@ -554,3 +554,51 @@ void orc_prefetch_weights(int64_t wbytes, const orc_plan_t *p, const int32_t *ws
             memcpy(pool + (int64_t)wslot[j] * wbytes, w_home + (int64_t)p->rep_expert[j] * wbytes,
                    (size_t)wbytes);
 }
+
+/* ------------------------------------------------------------------------ */
+/* Step 9: expert compute over the expert-grouped buffer.  [NCIJ] three-     */
+/* property list: views of the buffer go straight to the computation, which  */
+/* reads each rank's rows grouped by expert; "memory" panel: a replica's     */
+/* weights are in its prefetch slot, or, past B slots, at the home expert.   */
+/* One projection (a grouped GEMM):                                          */
+/*   y[r, n] = bf16( sum_k x[r, k] * W(r)[n, k] )   (fp64 sum, k ascending)  */
+/* for buffer row r = d*C + local, where W(r) is the [out_dim, in_dim]       */
+/* matrix at element w_offset of the weight row of r's segment:              */
+/*   home expert e of rank d holding local  -> w_home row e;                 */
+/*   replica j hosted on d holding local    -> pool row wslot[j] if >= 0,    */
+/*                                             else w_home row rep_expert[j].*/
+/* Weight rows are w_stride bf16 elements apart.  Only the listed rows are   */
+/* computed (the full product is too slow for a plain CPU loop at scale).    */
+/* ------------------------------------------------------------------------ */
+
+void orc_expert_gemm_rows(int32_t R, int32_t E, int32_t S, int32_t K, const orc_plan_t *p,
+                          const int32_t *wslot, int32_t in_dim, int32_t out_dim, const uint16_t *x,
+                          const uint16_t *w_home, const uint16_t *pool, int64_t w_stride,
+                          int64_t w_offset, int64_t nrows, const int64_t *rows, uint16_t *y)
+{
+    const int32_t L = E / R;
+    const int64_t C = (int64_t)S * K;
+    for (int64_t i = 0; i < nrows; ++i) {
+        const int64_t r = rows[i];
+        const int32_t d = (int32_t)(r / C);
+        const int64_t local = r - (int64_t)d * C;
+        const uint16_t *w = NULL;
+        for (int32_t e = d * L; e < (d + 1) * L && !w; ++e)
+            if (local >= p->home_row_off[e] && local < p->home_row_off[e] + p->keep[e])
+                w = w_home + (int64_t)e * w_stride;
+        for (int32_t j = 0; j < p->n_rep && !w; ++j)
+            if (p->rep_host[j] == d && local >= p->rep_row_off[j] &&
+                local < p->rep_row_off[j] + p->rep_count[j])
+                w = wslot[j] >= 0 ? pool + (int64_t)wslot[j] * w_stride
+                                  : w_home + (int64_t)p->rep_expert[j] * w_stride;
+        for (int32_t n = 0; n < out_dim; ++n) {
+            double acc = 0.0;
+            if (w) {
+                const uint16_t *wn = w + w_offset + (int64_t)n * in_dim;
+                for (int32_t k = 0; k < in_dim; ++k)
+                    acc += orc_bf16_to_double(x[r * in_dim + k]) * orc_bf16_to_double(wn[k]);
+            }
+            y[i * out_dim + n] = orc_bf16_from_double(acc);
+        }
+    }
+}

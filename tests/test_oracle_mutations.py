@@ -51,6 +51,15 @@ MUTANTS = {
     "weight_slot_counts_other_ranks": ("            if (p->rep_host[j] != d)\n                continue;",
                                        "            if (p->rep_host[j] != d && ++b)\n                continue;"),
     "prefetch_wrong_source": ("w_home + (int64_t)p->rep_expert[j] * wbytes", "w_home + (int64_t)p->rep_host[j] * wbytes"),
+    "gemm_ignores_wslot": ("w = wslot[j] >= 0 ? pool", "w = wslot[j] < -1 ? pool"),
+    "gemm_transposed_weight": ("acc += orc_bf16_to_double(x[r * in_dim + k]) * orc_bf16_to_double(wn[k]);",
+                               "acc += orc_bf16_to_double(x[r * in_dim + k]) * orc_bf16_to_double(w[w_offset + (int64_t)k * out_dim + n]);"),
+    "gemm_ignores_offset": ("const uint16_t *wn = w + w_offset + (int64_t)n * in_dim;",
+                            "const uint16_t *wn = w + (int64_t)n * in_dim;"),
+    "gemm_drops_last_k": ("for (int32_t k = 0; k < in_dim; ++k)\n                    acc",
+                          "for (int32_t k = 0; k + 1 < in_dim; ++k)\n                    acc"),
+    "gemm_home_range_off_by_one": ("local < p->home_row_off[e] + p->keep[e])\n                w = w_home",
+                                   "local <= p->home_row_off[e] + p->keep[e])\n                w = w_home"),
     "reduce_skips_home": ("double acc = (double)home[(int64_t)e * G + i];\n            for (int32_t q",
                           "double acc = 0.0;\n            for (int32_t q"),
     "reduce_keeps_replicas": ("rep[(int64_t)q * G + i] = 0.0f;", "rep[(int64_t)q * G + i] = rep[(int64_t)q * G + i];"),

@@ -782,3 +782,107 @@ def test_prefetch_is_a_gather_of_expert_rows():
         js = np.nonzero(ws[:pl.n_rep] >= 0)[0]
         want[ws[js]] = w_home[pl.rep_expert[js]]
         np.testing.assert_array_equal(pool, want)
+
+
+# ---------------------------------------------------------------------------
+# Expert compute over the grouped buffer (one projection, a grouped GEMM)
+# ---------------------------------------------------------------------------
+
+def bf16_of_f64_exact(v):
+    """bf16 bits of values that are exact in fp32 (torch's nearest-even cast)."""
+    t = torch.from_numpy(np.asarray(v, dtype=np.float64).astype(np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def small_plan(w, seed):
+    topk, _ = synth.routing(w, seed)
+    T, _ = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
+    slot_of, src_of_slot = oracle.slots(w.R, w.E, w.S, w.K, topk, pl)
+    return topk, pl, slot_of, src_of_slot
+
+
+@pytest.mark.parametrize("B_kind", ["none", "all"])
+def test_expert_gemm_picks_each_rows_weights(B_kind):
+    # W_e = 2^(e mod 4) * I; pool slots hold twice their expert's matrix, so a
+    # row reads x * 2^(e mod 4) at home or on an overflow replica and twice
+    # that on a slotted replica.  The row's expert comes from the slot maps
+    # and the routing, not from the segment table.
+    w = synth.Workload("g", 4, 8, 24, 2, 16, "zipf", alpha=1.8)
+    topk, pl, slot_of, src_of_slot = small_plan(w, 2)
+    assert pl.n_rep > 0
+    D = 16
+    B = 0 if B_kind == "none" else max(1, pl.max_rep_rank)
+    ws = oracle.weight_slots(w.R, w.E, B, pl)
+    eye = np.eye(D)
+    w_home = np.stack([bf16_of_f64_exact(eye * 2.0 ** (e % 4)).ravel() for e in range(w.E)])
+    pool = np.zeros((max(w.R * B, 1), D * D), np.uint16)
+    for j in range(pl.n_rep):
+        if ws[j] >= 0:
+            pool[ws[j]] = bf16_of_f64_exact(eye * 2.0 ** (pl.rep_expert[j] % 4 + 1)).ravel()
+    x = synth.normal_bf16(3, synth.TAG_X, w.NK * D).reshape(w.NK, D)
+    y = oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, ws, D, D, x, w_home, pool, D * D)
+    xf = bf16_bits_to_f64(x)
+    home_rows = np.zeros(w.NK, bool)
+    for d in range(w.R):
+        n_home = sum(int(pl.keep[e]) for e in range(d * (w.E // w.R), (d + 1) * (w.E // w.R)))
+        home_rows[d * w.C:d * w.C + n_home] = True
+    e_row = topk[src_of_slot]
+    factor = 2.0 ** (e_row % 4) * np.where(home_rows | (B == 0), 1.0, 2.0)
+    np.testing.assert_array_equal(y, bf16_of_f64_exact(xf * factor[:, None]))
+
+
+def test_expert_gemm_integer_inputs_equal_matmul():
+    # small integers: every product and sum is exact, so y = bf16(exact) for
+    # each segment's x_rows @ W^T (numpy), with a projection offset in the row
+    rng = np.random.default_rng(9)
+    w = synth.Workload("g", 2, 4, 20, 2, 8, "zipf", alpha=1.5)
+    topk, pl, slot_of, src_of_slot = small_plan(w, 4)
+    assert pl.n_rep > 0
+    kin, kout, off = 24, 40, 7 * 24
+    stride = off + kout * kin + 5
+    B = 1
+    ws = oracle.weight_slots(w.R, w.E, B, pl)
+    W = rng.integers(-4, 5, (w.E, kout, kin)).astype(np.float64)
+    Wp = rng.integers(-4, 5, (w.R * B, kout, kin)).astype(np.float64)
+    X = rng.integers(-4, 5, (w.NK, kin)).astype(np.float64)
+    w_home = np.zeros((w.E, stride), np.uint16)
+    w_home[:, off:off + kout * kin] = bf16_of_f64_exact(W.reshape(w.E, -1))
+    pool = np.zeros((w.R * B, stride), np.uint16)
+    pool[:, off:off + kout * kin] = bf16_of_f64_exact(Wp.reshape(w.R * B, -1))
+    y = oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, ws, kin, kout, bf16_of_f64_exact(X), w_home,
+                           pool, stride, off)
+    want = np.empty((w.NK, kout))
+    L = w.E // w.R
+    for d in range(w.R):
+        for e in range(d * L, (d + 1) * L):
+            r0 = d * w.C + pl.home_row_off[e]
+            want[r0:r0 + pl.keep[e]] = X[r0:r0 + pl.keep[e]] @ W[e].T
+        for j in range(pl.n_rep):
+            if pl.rep_host[j] == d:
+                r0 = d * w.C + pl.rep_row_off[j]
+                Wj = Wp[ws[j]] if ws[j] >= 0 else W[pl.rep_expert[j]]
+                want[r0:r0 + pl.rep_count[j]] = X[r0:r0 + pl.rep_count[j]] @ Wj.T
+    np.testing.assert_array_equal(y, bf16_of_f64_exact(want))
+    # listed rows only: same values
+    rows = np.array([0, 5, w.NK - 1], dtype=np.int64)
+    np.testing.assert_array_equal(
+        oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, ws, kin, kout, bf16_of_f64_exact(X), w_home,
+                           pool, stride, off, rows=rows), y[rows])
+
+
+def test_expert_gemm_rounds_the_exact_sum_once():
+    # one row, one output: x = [1, 2^-9, 2^-9], w = [1, 1, 1] -> 1 + 2^-8 is a
+    # bf16 tie between 1 and 1 + 2^-7: even gives 1; a fourth 2^-9 term
+    # breaks the tie upward
+    w = synth.Workload("g", 1, 1, 1, 1, 8, "zipf")
+    topk = np.zeros(1, np.int32)
+    T, _ = oracle.route_stats(1, 1, 1, 1, topk)
+    pl = oracle.plan(1, 1, 1, 1, T)
+    ws = oracle.weight_slots(1, 1, 0, pl)
+    for tail, want in ((2, 1.0), (3, 1.0 + 2.0 ** -7)):
+        xs = [1.0] + [2.0 ** -9] * tail
+        x = bf16_of_f64_exact(np.array([xs]))
+        wv = bf16_of_f64_exact(np.ones((1, len(xs))))
+        y = oracle.expert_gemm(1, 1, 1, 1, pl, ws, len(xs), 1, x, wv, None, len(xs))
+        assert y[0, 0] == bf16_of_f64_exact(np.array([want]))[0]
