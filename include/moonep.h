@@ -236,6 +236,29 @@ int moonep_prefetch_weights(const moonep_shape *shape, const int32_t *plan, cons
                             void *stream);
 
 /*
+ * Expert compute over the expert-grouped buffer: one projection, a grouped
+ * GEMM [NCIJ three-property list: buffer views go straight to the
+ * computation, each rank's rows grouped by expert; explainer "memory" panel:
+ * replicas read their prefetch slot, or the home expert past B slots].
+ * x: bf16 [R*S*K, in_dim], the buffer rows (e.g. the dispatch buffer);
+ * y: bf16 [R*S*K, out_dim].  For buffer row r of rank d = r div (S*K):
+ *   y[r, n] = bf16( sum_k x[r, k] * W[n, k] )  (fp32 accumulation on the
+ *             matrix cores, one rounding to nearest even),
+ * where W is the [out_dim, in_dim] row-major matrix starting at element
+ * w_offset of the weight row of r's segment: w_home + e*w_stride for a home
+ * expert e; for replica j, pool + wslot[j]*w_stride when 0 <= wslot[j] < R*B,
+ * else w_home + rep_expert[j]*w_stride.  w_home holds E weight rows, pool R*B
+ * (the layouts of moonep_prefetch_weights, counted in bf16 elements here).
+ * Limits (else MOONEP_ERR_ARG): in_dim % 64 == 0, out_dim % 128 == 0,
+ * w_stride and w_offset multiples of 8, w_offset + out_dim*in_dim <= w_stride.
+ * x, y, w_home, pool 16-byte aligned; y must not overlap x, w_home or pool.
+ */
+int moonep_expert_gemm(const moonep_shape *shape, const int32_t *plan, const int32_t *wslot,
+                       int32_t B, int32_t in_dim, int32_t out_dim, const uint16_t *x,
+                       const uint16_t *w_home, const uint16_t *pool, int64_t w_stride,
+                       int64_t w_offset, uint16_t *y, void *stream);
+
+/*
  * Reads the sticky device error word of a workspace into *host_code, then
  * clears it.  Synchronises `stream`.  The only call that waits for the device.
  */

@@ -31,7 +31,7 @@ EXPORTS = ("moonep_check_shape", "moonep_workspace_bytes", "moonep_plan_layout_o
            "moonep_plan_bytes", "moonep_route_stats", "moonep_plan", "moonep_dispatch",
            "moonep_combine", "moonep_combine_bwd", "moonep_dispatch_bwd",
            "moonep_replica_grad_reduce", "moonep_weight_slots", "moonep_prefetch_weights",
-           "moonep_read_error")
+           "moonep_expert_gemm", "moonep_read_error")
 
 
 class MoonepError(RuntimeError):
@@ -93,6 +93,8 @@ def lib():
             "moonep_replica_grad_reduce": (ctypes.c_int, [P, VP, I64, VP, VP, VP]),
             "moonep_weight_slots": (ctypes.c_int, [P, VP, ctypes.c_int32, VP, VP]),
             "moonep_prefetch_weights": (ctypes.c_int, [P, VP, VP, ctypes.c_int32, I64, VP, VP, VP]),
+            "moonep_expert_gemm": (ctypes.c_int, [P, VP, VP, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int32, VP, VP, VP, I64, I64, VP, VP]),
             "moonep_read_error": (ctypes.c_int, [VP, SZ, ctypes.POINTER(ctypes.c_int32), VP]),
         }
         for name, (res, args) in sig.items():
@@ -263,6 +265,19 @@ def moonep_prefetch_weights(shape, plan, wslot, B, wbytes, w_home, pool, stream=
         _dev_bytes(w_home, "w_home", shape.E * wbytes),
         _dev_bytes(pool, "pool", shape.R * B * wbytes), _stream(stream)),
         "moonep_prefetch_weights")
+
+
+def moonep_expert_gemm(shape, plan, wslot, B, in_dim, out_dim, x, w_home, pool, w_stride,
+                       w_offset, y, stream=None):
+    """y [R*S*K, out_dim] = each buffer row of x [R*S*K, in_dim] times its
+    segment's weights; w_home [E, w_stride] and pool [R*B, w_stride] bf16."""
+    _check(lib().moonep_expert_gemm(
+        ctypes.byref(shape), _dev(plan, "plan", moonep_plan_bytes(shape) // 4, ("int32",)),
+        _dev(wslot, "wslot", shape.E + shape.R, ("int32",)), int(B), int(in_dim), int(out_dim),
+        _dev(x, "x", shape.NK * in_dim, _BF16_OK),
+        _dev_bytes(w_home, "w_home", shape.E * w_stride * 2),
+        _dev_bytes(pool, "pool", shape.R * B * w_stride * 2), int(w_stride), int(w_offset),
+        _dev(y, "y", shape.NK * out_dim, _BF16_OK), _stream(stream)), "moonep_expert_gemm")
 
 
 def moonep_read_error(workspace, stream=None) -> int:

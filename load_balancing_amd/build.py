@@ -10,7 +10,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoonep.so")
-SOURCES = ["abi.hip", "route_stats.hip", "plan.hip", "movers.hip", "reduce.hip", "prefetch.hip"]
+SOURCES = ["abi.hip", "route_stats.hip", "plan.hip", "movers.hip", "reduce.hip", "prefetch.hip", "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

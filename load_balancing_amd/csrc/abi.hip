@@ -28,6 +28,11 @@ int launch_weight_slots(const moonep_shape &s, const int32_t *plan, int32_t B, i
                         hipStream_t st);
 int launch_prefetch(const moonep_shape &s, const int32_t *plan, const int32_t *wslot, int32_t B,
                     int64_t wbytes, const void *w_home, void *pool, int grid, hipStream_t st);
+int gemm_out_align();
+int launch_expert_gemm(const moonep_shape &s, const int32_t *plan, const int32_t *wslot, int32_t B,
+                       int32_t in_dim, int32_t out_dim, const uint16_t *x, const uint16_t *w_home,
+                       const uint16_t *pool, int64_t w_stride, int64_t w_offset, uint16_t *y,
+                       hipStream_t st);
 }  // namespace moonep
 
 using namespace moonep;
@@ -285,6 +290,35 @@ int moonep_prefetch_weights(const moonep_shape *shape, const int32_t *plan, cons
         return MOONEP_ERR_HIP;
     return launch_prefetch(*shape, plan, wslot, B, wbytes, w_home, pool, cus * 4,
                            (hipStream_t)stream);
+}
+
+int moonep_expert_gemm(const moonep_shape *shape, const int32_t *plan, const int32_t *wslot,
+                       int32_t B, int32_t in_dim, int32_t out_dim, const uint16_t *x,
+                       const uint16_t *w_home, const uint16_t *pool, int64_t w_stride,
+                       int64_t w_offset, uint16_t *y, void *stream)
+{
+    int rc = shape_status(shape);
+    if (rc != MOONEP_OK)
+        return rc;
+    if (B < 0 || (int64_t)shape->R * B >= ((int64_t)1 << 31) || in_dim <= 0 || in_dim % 64 != 0 ||
+        out_dim <= 0 || out_dim % gemm_out_align() != 0 || w_stride % 8 != 0 || w_offset < 0 ||
+        w_offset % 8 != 0 || w_offset + (int64_t)out_dim * in_dim > w_stride)
+        return MOONEP_ERR_ARG;
+    const int64_t rows = n_entries(shape);
+    const int64_t pool_rows = (int64_t)shape->R * B;
+    if (!plan || !wslot || !w_home || !present(x, rows) || !present(y, rows) ||
+        !present(pool, pool_rows))
+        return MOONEP_ERR_NULL_PTR;
+    if (!aligned(plan, 4) || !aligned(wslot, 4) || !aligned(x, 16) || !aligned(y, 16) ||
+        !aligned(w_home, 16) || !aligned(pool, 16))
+        return MOONEP_ERR_MISALIGNED;
+    const size_t yb = (size_t)rows * out_dim * 2;
+    if (overlap(y, yb, x, (size_t)rows * in_dim * 2) ||
+        overlap(y, yb, w_home, (size_t)shape->E * (size_t)w_stride * 2) ||
+        overlap(y, yb, pool, (size_t)pool_rows * (size_t)w_stride * 2))
+        return MOONEP_ERR_ALIAS;
+    return launch_expert_gemm(*shape, plan, wslot, B, in_dim, out_dim, x, w_home, pool, w_stride,
+                              w_offset, y, (hipStream_t)stream);
 }
 
 int moonep_read_error(void *workspace, size_t workspace_bytes, int32_t *host_code, void *stream)

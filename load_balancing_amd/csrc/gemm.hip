@@ -1,0 +1,343 @@
+// gemm.hip -- expert compute over the expert-grouped buffer: one projection,
+// a grouped GEMM on the matrix cores.
+//
+// The MoonEP article (ncijnetwork.com), three-property list: views of the
+// static buffer go straight to the computation, which finds each rank's rows
+// grouped by expert (home experts, then the replicas the rank hosts).  Its
+// explainer "memory" panel: a replica's weights sit in its prefetch slot, or,
+// past the B slots, are read at the home expert.
+//
+//   y[r, n] = bf16( sum_k x[r, k] * W(r)[n, k] )
+//
+// with W(r) the [out_dim, in_dim] matrix at element w_offset of the weight row
+// of r's segment.  A segment is a home expert (rows home_row_off[e] .. + keep[e]
+// of rank e div L) or a replica (rows rep_row_off[j] .. + rep_count[j] of its
+// host).  Segments are cut into tiles of BM rows that never cross a segment,
+// so every tile multiplies by one weight matrix.
+//
+// Kernel: a persistent grid.  Every workgroup first scans the per-segment tile
+// counts into LDS (n_rep is known only on the device), then walks
+// (tile, column-block) items.  The items of each XCD are one contiguous range,
+// so the workgroups running together on one XCD share their row tile and the
+// segment's weights in that XCD's L2.  Per item: BM x BN outputs, K in steps
+// of 64 through double-buffered, padded LDS tiles; each wave computes 64 x 64
+// with 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators (fp32), then the tile is
+// rounded to bf16 (nearest even) and stored through LDS as 16-byte rows.
+//
+// MFMA lane layouts (checked on gfx950): operand A lane l holds row l % 32,
+// k = (l / 32) * 8 .. + 7; operand B lane l holds column l % 32, same k; the
+// 32 x 32 fp32 result holds, in lane l and register r, row
+// (r / 4) * 8 + (l / 32) * 4 + r % 4 and column l % 32.
+#include "moonep_internal.hpp"
+
+namespace moonep {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+template <int BM, int BN>
+struct GemmCfg {
+    static constexpr int kBK = 64;                  // k per LDS stage
+    static constexpr int kWM = BM / 64, kWN = BN / 64;
+    static constexpr int kWavesG = kWM * kWN;
+    static constexpr int kThreads = kWavesG * 64;
+    static constexpr int kLdk = kBK + 8;            // padded LDS row, elements
+    static constexpr int kStage = (BM + BN) * kLdk; // elements per stage
+    static constexpr int kAVec = BM * 8 / kThreads; // 16-byte loads per thread
+    static constexpr int kBVec = BN * 8 / kThreads;
+    static constexpr int kLdo = BN + 8;             // epilogue LDS row, elements
+    static constexpr int kOVec = BM * BN / 8 / kThreads;
+    static_assert(BM * (BN + 8) <= 2 * kStage, "epilogue must fit the stages");
+    static_assert(kAVec >= 1 && kBVec >= 1 && kOVec >= 1, "tile too small for the block");
+};
+
+// Exclusive scan of one int per thread over a block of NW waves.
+template <int NW>
+__device__ __forceinline__ int block_scan_excl(int v, int *tmp, int *total)
+{
+    const int lane = lane_id(), wid = (int)threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d, 64);
+        if (lane >= d)
+            incl += o;
+    }
+    if (lane == 63)
+        tmp[wid] = incl;
+    __syncthreads();
+    int base = 0, sum = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int t = tmp[w];
+        base += w < wid ? t : 0;
+        sum += t;
+    }
+    __syncthreads();
+    *total = sum;
+    return base + incl - v;
+}
+
+struct GemmArgs {
+    const int32_t *plan;
+    PlanLayout pl;
+    const int32_t *wslot;
+    int32_t R, E, L, C, nslots;
+    int32_t in_dim, out_dim;
+    const uint16_t *x, *w_home, *pool;
+    int64_t w_stride, w_offset;
+    uint16_t *y;
+};
+
+template <int BM, int BN>
+__global__ __launch_bounds__((GemmCfg<BM, BN>::kThreads)) void expert_gemm_kernel(GemmArgs a)
+{
+    using G = GemmCfg<BM, BN>;
+    extern __shared__ __align__(16) uint16_t lds[];
+    uint16_t *stage0 = lds;
+    int32_t *seg_start = (int32_t *)(lds + 2 * G::kStage);  // [E + cap + 1]
+    __shared__ int scan_tmp[G::kWavesG];
+
+    const int tid = (int)threadIdx.x, lane = lane_id(), wave = tid >> 6;
+    const int32_t cap = a.pl.cap;
+    const int32_t nr_raw = a.plan[a.pl.header + MOONEP_PLAN_H_N_REP];
+    const int32_t n_rep = nr_raw < 0 ? 0 : (nr_raw < cap ? nr_raw : cap);
+    const int32_t nseg = a.E + n_rep;
+
+    // ---- segment tile counts, scanned into seg_start ----------------------
+    // segment s < E: home expert s; s >= E: replica s - E.  A bad table entry
+    // makes an empty segment, so every access below stays in bounds.
+    auto seg_len = [&](int32_t s) -> int32_t {
+        if (s < a.E) {
+            const int32_t off = a.plan[a.pl.home_row_off + s], n = a.plan[a.pl.keep + s];
+            return (off >= 0 && n >= 0 && off <= a.C - n) ? n : 0;
+        }
+        const int32_t j = s - a.E;
+        const int32_t h = a.plan[a.pl.rep_host + j], e = a.plan[a.pl.rep_expert + j];
+        const int32_t off = a.plan[a.pl.rep_row_off + j], n = a.plan[a.pl.rep_count + j];
+        return (h >= 0 && h < a.R && e >= 0 && e < a.E && off >= 0 && n >= 0 && off <= a.C - n)
+                   ? n : 0;
+    };
+    const int32_t per = (nseg + G::kThreads - 1) / G::kThreads;
+    const int32_t s0 = tid * per;
+    int32_t mine = 0;
+    for (int32_t s = s0; s < s0 + per && s < nseg; ++s) {
+        const int32_t len = seg_len(s);
+        mine += len > 0 ? (len + BM - 1) / BM : 0;
+    }
+    int32_t total_tiles = 0;
+    int32_t run = block_scan_excl<G::kWavesG>(mine, scan_tmp, &total_tiles);
+    for (int32_t s = s0; s < s0 + per && s < nseg; ++s) {
+        seg_start[s] = run;
+        const int32_t len = seg_len(s);
+        run += len > 0 ? (len + BM - 1) / BM : 0;
+    }
+    if (tid == 0)
+        seg_start[nseg] = total_tiles;
+    __syncthreads();
+
+    // ---- items of this workgroup's XCD -------------------------------------
+    const int32_t nbn = a.out_dim / BN;
+    const int64_t items = (int64_t)total_tiles * nbn;
+    const int xcd = (int)(blockIdx.x % 8), q = (int)(blockIdx.x / 8);
+    const int gx = ((int)gridDim.x - xcd + 7) / 8;
+    const int64_t span = (items + 7) / 8;
+    const int64_t lo = (int64_t)xcd * span;
+    const int64_t hi = lo + span < items ? lo + span : items;
+    const int32_t nk = a.in_dim / G::kBK;
+    const int wm = wave / G::kWN, wn = wave % G::kWN;
+    int log_nseg = 0;
+    while ((1 << log_nseg) < nseg + 1)
+        ++log_nseg;
+
+    for (int64_t it = lo + q; it < hi; it += gx) {
+        const int32_t t = (int32_t)(it / nbn);
+        const int32_t nb = (int32_t)(it - (int64_t)t * nbn);
+        // segment holding tile t: last s with seg_start[s] <= t (fixed-depth search)
+        int32_t s = 0;
+        for (int b = log_nseg - 1; b >= 0; --b) {
+            const int32_t c = s + (1 << b);
+            if (c < nseg && seg_start[c] <= t)
+                s = c;
+        }
+        const int32_t mt = t - seg_start[s];
+        int64_t row0;
+        int32_t len;
+        const uint16_t *wbase;
+        if (s < a.E) {
+            row0 = (int64_t)(s / a.L) * a.C + a.plan[a.pl.home_row_off + s];
+            len = seg_len(s);
+            wbase = a.w_home + (int64_t)s * a.w_stride;
+        } else {
+            const int32_t j = s - a.E;
+            row0 = (int64_t)a.plan[a.pl.rep_host + j] * a.C + a.plan[a.pl.rep_row_off + j];
+            len = seg_len(s);
+            const int32_t ws = a.wslot[j];
+            wbase = (ws >= 0 && ws < a.nslots)
+                        ? a.pool + (int64_t)ws * a.w_stride
+                        : a.w_home + (int64_t)a.plan[a.pl.rep_expert + j] * a.w_stride;
+        }
+        wbase += a.w_offset;
+        const int64_t m0 = row0 + (int64_t)mt * BM;
+        const int32_t mrows = len - mt * BM < BM ? len - mt * BM : BM;
+        const int64_t n0 = (int64_t)nb * BN;
+
+        // global -> register loads of one k stage
+        u32x4 ra[G::kAVec], rb[G::kBVec];
+        auto load = [&](int32_t kt) {
+            const int64_t k0 = (int64_t)kt * G::kBK;
+#pragma unroll
+            for (int v = 0; v < G::kAVec; ++v) {
+                const int idx = tid + v * G::kThreads;
+                const int row = idx >> 3, c = idx & 7;
+                const int64_t gr = m0 + (row < mrows ? row : 0);
+                ra[v] = *(const u32x4 *)(a.x + gr * a.in_dim + k0 + c * 8);
+            }
+#pragma unroll
+            for (int v = 0; v < G::kBVec; ++v) {
+                const int idx = tid + v * G::kThreads;
+                const int row = idx >> 3, c = idx & 7;
+                rb[v] = *(const u32x4 *)(wbase + (n0 + row) * a.in_dim + k0 + c * 8);
+            }
+        };
+        auto store = [&](uint16_t *st) {
+#pragma unroll
+            for (int v = 0; v < G::kAVec; ++v) {
+                const int idx = tid + v * G::kThreads;
+                *(u32x4 *)(st + (idx >> 3) * G::kLdk + (idx & 7) * 8) = ra[v];
+            }
+            uint16_t *sb = st + BM * G::kLdk;
+#pragma unroll
+            for (int v = 0; v < G::kBVec; ++v) {
+                const int idx = tid + v * G::kThreads;
+                *(u32x4 *)(sb + (idx >> 3) * G::kLdk + (idx & 7) * 8) = rb[v];
+            }
+        };
+
+        f32x16 acc[2][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    acc[i][j][r] = 0.0f;
+
+        load(0);
+        store(stage0);
+        __syncthreads();
+        for (int32_t kt = 0; kt < nk; ++kt) {
+            if (kt + 1 < nk)
+                load(kt + 1);
+            const uint16_t *sa = stage0 + (kt & 1) * G::kStage;
+            const uint16_t *sb = sa + BM * G::kLdk;
+#pragma unroll
+            for (int ks = 0; ks < G::kBK / 16; ++ks) {
+                const int kof = ks * 16 + (lane >> 5) * 8;
+                bf16x8 fa[2], fb[2];
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+                    fa[i] = *(const bf16x8 *)(sa + (wm * 64 + i * 32 + (lane & 31)) * G::kLdk + kof);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    fb[j] = *(const bf16x8 *)(sb + (wn * 64 + j * 32 + (lane & 31)) * G::kLdk + kof);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
+                                                                            0, 0, 0);
+            }
+            if (kt + 1 < nk)
+                store(stage0 + ((kt + 1) & 1) * G::kStage);
+            __syncthreads();
+        }
+
+        // ---- epilogue: bf16 tile through LDS, 16-byte row stores -------------
+        uint16_t *so = stage0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                    const int col = wn * 64 + j * 32 + (lane & 31);
+                    const uint32_t p = pack_bf16(acc[i][j][r], acc[i][j][r + 1]);
+                    so[row * G::kLdo + col] = (uint16_t)(p & 0xFFFFu);
+                    so[(row + 1) * G::kLdo + col] = (uint16_t)(p >> 16);
+                }
+        __syncthreads();
+#pragma unroll
+        for (int v = 0; v < G::kOVec; ++v) {
+            const int idx = tid + v * G::kThreads;
+            const int row = idx / (BN / 8), c = idx % (BN / 8);
+            if (row < mrows)
+                *(u32x4 *)(a.y + (m0 + row) * a.out_dim + n0 + c * 8) =
+                    *(const u32x4 *)(so + row * G::kLdo + c * 8);
+        }
+        __syncthreads();
+    }
+}
+
+namespace {
+
+template <int BM, int BN>
+int run_gemm(const GemmArgs &ga, hipStream_t st)
+{
+    using G = GemmCfg<BM, BN>;
+    const size_t lds = (size_t)2 * G::kStage * 2 + (size_t)(ga.E + ga.pl.cap + 1) * 4;
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return MOONEP_ERR_HIP;
+    static bool raised[64] = {};
+    if (dev >= 0 && dev < 64 && !raised[dev]) {
+        if (hipFuncSetAttribute((const void *)expert_gemm_kernel<BM, BN>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+            return MOONEP_ERR_HIP;
+        raised[dev] = true;
+    }
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (expert_gemm_kernel<BM, BN>),
+                                                     G::kThreads, lds) != hipSuccess)
+        return MOONEP_ERR_HIP;
+    const int grid = cus * (per_cu > 0 ? per_cu : 1);
+    hipLaunchKernelGGL((expert_gemm_kernel<BM, BN>), dim3(grid), dim3(G::kThreads), lds, st, ga);
+    return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
+}
+
+}  // namespace
+
+constexpr int kGemmBM = 128, kGemmBN = 128;
+
+int gemm_out_align() { return kGemmBN; }
+
+int launch_expert_gemm(const moonep_shape &s, const int32_t *plan, const int32_t *wslot, int32_t B,
+                       int32_t in_dim, int32_t out_dim, const uint16_t *x, const uint16_t *w_home,
+                       const uint16_t *pool, int64_t w_stride, int64_t w_offset, uint16_t *y,
+                       hipStream_t st)
+{
+    if ((int64_t)s.R * s.S * s.K == 0)
+        return MOONEP_OK;
+    GemmArgs ga;
+    ga.plan = plan;
+    ga.pl = plan_layout(s.E, s.R);
+    ga.wslot = wslot;
+    ga.R = s.R;
+    ga.E = s.E;
+    ga.L = s.E / s.R;
+    ga.C = s.S * s.K;
+    ga.nslots = s.R * B;
+    ga.in_dim = in_dim;
+    ga.out_dim = out_dim;
+    ga.x = x;
+    ga.w_home = w_home;
+    ga.pool = pool;
+    ga.w_stride = w_stride;
+    ga.w_offset = w_offset;
+    ga.y = y;
+    return run_gemm<kGemmBM, kGemmBN>(ga, st);
+}
+
+}  // namespace moonep

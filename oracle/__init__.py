@@ -106,7 +106,7 @@ def lib():
         L.orc_replica_grad_reduce_at.argtypes = [i32, ctypes.POINTER(_CPlan), i64, p, p, i64, p]
         L.orc_expert_gemm_rows.restype = None
         L.orc_expert_gemm_rows.argtypes = [i32, i32, i32, i32, ctypes.POINTER(_CPlan), p, i32, i32,
-                                           p, p, p, i64, i64, i64, p, p]
+                                           p, p, p, i64, i64, i64, p, i32, p]
         L.orc_weight_slots.restype = None
         L.orc_weight_slots.argtypes = [i32, i32, i32, ctypes.POINTER(_CPlan), p]
         L.orc_prefetch_weights.restype = None
@@ -305,9 +305,10 @@ def prefetch_weights(pl: Plan, wslot, w_home, pool):
 
 
 def expert_gemm(R, E, S, K, pl: Plan, wslot, in_dim, out_dim, x, w_home, pool, w_stride,
-                w_offset=0, rows=None):
+                w_offset=0, rows=None, x_compact=False):
     """y [len(rows), out_dim] bf16 bits: one projection of the listed buffer rows
-    (all R*S*K rows if rows is None) by their segment's weight matrix."""
+    (all R*S*K rows if rows is None) by their segment's weight matrix.  With
+    x_compact, x holds only the listed rows, in order."""
     x = _c(x, np.uint16)
     w_home = _c(w_home, np.uint16)
     pool = _c(pool, np.uint16) if pool is not None and np.size(pool) else np.zeros(1, np.uint16)
@@ -317,7 +318,7 @@ def expert_gemm(R, E, S, K, pl: Plan, wslot, in_dim, out_dim, x, w_home, pool, w
     c = _cplan_from(pl)
     lib().orc_expert_gemm_rows(R, E, S, K, ctypes.byref(c), _p(wslot), in_dim, out_dim, _p(x),
                                _p(w_home), _p(pool), w_stride, w_offset, rows.size, _p(rows),
-                               _p(y))
+                               int(bool(x_compact)), _p(y))
     return y
 
 

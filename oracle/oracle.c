@@ -568,13 +568,15 @@ void orc_prefetch_weights(int64_t wbytes, const orc_plan_t *p, const int32_t *ws
 /*   replica j hosted on d holding local    -> pool row wslot[j] if >= 0,    */
 /*                                             else w_home row rep_expert[j].*/
 /* Weight rows are w_stride bf16 elements apart.  Only the listed rows are   */
-/* computed (the full product is too slow for a plain CPU loop at scale).    */
+/* computed (the full product is too slow for a plain CPU loop at scale);    */
+/* with x_compact, x holds just those rows, in the order listed.             */
 /* ------------------------------------------------------------------------ */
 
 void orc_expert_gemm_rows(int32_t R, int32_t E, int32_t S, int32_t K, const orc_plan_t *p,
                           const int32_t *wslot, int32_t in_dim, int32_t out_dim, const uint16_t *x,
                           const uint16_t *w_home, const uint16_t *pool, int64_t w_stride,
-                          int64_t w_offset, int64_t nrows, const int64_t *rows, uint16_t *y)
+                          int64_t w_offset, int64_t nrows, const int64_t *rows, int32_t x_compact,
+                          uint16_t *y)
 {
     const int32_t L = E / R;
     const int64_t C = (int64_t)S * K;
@@ -591,12 +593,13 @@ void orc_expert_gemm_rows(int32_t R, int32_t E, int32_t S, int32_t K, const orc_
                 local < p->rep_row_off[j] + p->rep_count[j])
                 w = wslot[j] >= 0 ? pool + (int64_t)wslot[j] * w_stride
                                   : w_home + (int64_t)p->rep_expert[j] * w_stride;
+        const uint16_t *xr = x + (x_compact ? i : r) * in_dim;
         for (int32_t n = 0; n < out_dim; ++n) {
             double acc = 0.0;
             if (w) {
                 const uint16_t *wn = w + w_offset + (int64_t)n * in_dim;
                 for (int32_t k = 0; k < in_dim; ++k)
-                    acc += orc_bf16_to_double(x[r * in_dim + k]) * orc_bf16_to_double(wn[k]);
+                    acc += orc_bf16_to_double(xr[k]) * orc_bf16_to_double(wn[k]);
             }
             y[i * out_dim + n] = orc_bf16_from_double(acc);
         }

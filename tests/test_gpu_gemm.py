@@ -1,0 +1,177 @@
+"""GPU parity of the grouped expert GEMM (one projection over the grouped buffer).
+
+Integer-valued bf16 inputs make every partial sum exact in fp32, so the GPU
+must equal the oracle bit for bit whatever its accumulation order: that pins
+the tiling, the segment-to-weight mapping (home, slotted replica, overflow
+replica) and the ragged tiles.  Real-valued inputs are held to the bound of an
+fp32 accumulation rounded once to bf16:
+    |gpu - oracle| <= ulp_bf16(max(|gpu|, |oracle|)) + in_dim * 2^-23 * sum_k |x_k w_k|
+(half an ulp for each of the two roundings to bf16, plus twice the
+worst-case error of in_dim fp32 additions).  Full-size shapes are checked on
+sampled rows, and no output row may keep its sentinel.
+"""
+import numpy as np
+import pytest
+import torch
+
+import load_balancing_amd as mx
+import oracle
+import synth
+from gpu_harness import bf16_dev, bits, oracle_plan, shape_of, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def f64(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def bf16_of(v):
+    t = torch.from_numpy(np.asarray(v, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def setup(w, seed, B):
+    topk, _ = synth.routing(w, seed)
+    T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk)
+    s = shape_of(w)
+    b = mx.allocate(s)
+    mx.plan_step(b, to_dev(topk))
+    ws = torch.empty(w.E + w.R, dtype=torch.int32, device="cuda")
+    mx.moonep_weight_slots(s, b.plan, B, ws)
+    torch.cuda.synchronize()
+    o_ws = oracle.weight_slots(w.R, w.E, B, pl)
+    np.testing.assert_array_equal(ws.cpu().numpy(), o_ws)
+    return s, b, pl, ws, o_ws
+
+
+def run_gemm(s, b, ws, B, kin, kout, x, w_home, pool, stride, off):
+    y = torch.empty((s.NK, kout), dtype=torch.bfloat16, device="cuda")
+    y.view(torch.int16).fill_(-1)                       # sentinel (a NaN)
+    mx.moonep_expert_gemm(s, b.plan, ws, B, kin, kout, bf16_dev(x), to_dev(w_home.view(np.int16)),
+                          to_dev(pool.view(np.int16)), stride, off, y)
+    torch.cuda.synchronize()
+    return y
+
+
+def abs_products(w, pl, o_ws, rows, x_rows, w_home, pool, off, kin, kout):
+    """sum_k |x_k w_k| for every listed row and output (the error bound's scale),
+    through a test-side walk of the segment table; rows ascending, so one
+    segment's |W| is built once."""
+    C, L = w.C, w.E // w.R
+    A = np.empty((len(rows), kout))
+    key, Wabs = None, None
+    for i, r in enumerate(rows):
+        d, loc = divmod(int(r), C)
+        k = None
+        for e in range(d * L, (d + 1) * L):
+            if pl.home_row_off[e] <= loc < pl.home_row_off[e] + pl.keep[e]:
+                k = ("home", e)
+        for j in range(pl.n_rep):
+            if pl.rep_host[j] == d and pl.rep_row_off[j] <= loc < pl.rep_row_off[j] + pl.rep_count[j]:
+                k = ("pool", int(o_ws[j])) if o_ws[j] >= 0 else ("home", int(pl.rep_expert[j]))
+        if k != key:
+            src = w_home[k[1]] if k[0] == "home" else pool[k[1]]
+            Wabs = np.abs(f64(src[off:off + kout * kin]).reshape(kout, kin))
+            key = k
+        A[i] = Wabs @ np.abs(f64(x_rows[i]))
+    return A
+
+
+def check_bound(y_rows, o_rows, A, kin):
+    g, o = f64(y_rows), f64(o_rows)
+    mag = np.maximum(np.abs(g), np.abs(o))
+    ulp = np.where(mag > 0, 2.0 ** (np.floor(np.log2(np.maximum(mag, 1e-300))) - 7), 2.0 ** -133)
+    err = np.abs(g - o)
+    assert (err <= ulp + kin * 2.0 ** -23 * A).all(), f"max err {err.max()}"
+    return float((y_rows == o_rows).mean())
+
+
+SMALL = [
+    (synth.WORKLOADS["tiny"], 128, 256),
+    (synth.Workload("skew", 4, 16, 100, 4, 64, "zipf", alpha=2.5), 64, 128),
+    (synth.Workload("many_ranks", 16, 32, 64, 2, 64, "zipf", alpha=1.3), 192, 384),
+    (synth.Workload("one_rank", 1, 4, 50, 2, 64, "zipf", alpha=1.0), 64, 128),
+    (synth.Workload("adversarial_small", 8, 32, 64, 4, 64, "fixed", gates="uniform"), 128, 128),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: c[0].name)
+def test_gemm_integer_inputs_bit_exact(case):
+    w, kin, kout = case
+    rng = np.random.default_rng(1)
+    L = w.E // w.R
+    for B in sorted({0, 1, L}):
+        print(f"[case] {w.name} kin={kin} kout={kout} B={B}", flush=True)
+        s, b, pl, ws, o_ws = setup(w, 0, B)
+        off = 8 * 3
+        stride = off + kout * kin + 16
+        w_home = bf16_of(rng.integers(-4, 5, (w.E, stride)))
+        pool = bf16_of(rng.integers(-4, 5, (max(w.R * B, 0), stride)))
+        x = bf16_of(rng.integers(-4, 5, (w.NK, kin)))
+        y = run_gemm(s, b, ws, B, kin, kout, x, w_home, pool, stride, off)
+        want = oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, o_ws, kin, kout, x, w_home, pool,
+                                  stride, off)
+        np.testing.assert_array_equal(bits(y), want)
+
+
+@pytest.mark.parametrize("case", SMALL[:3], ids=lambda c: c[0].name)
+def test_gemm_real_inputs_within_bound(case):
+    w, kin, kout = case
+    B = 1
+    print(f"[case] {w.name} real kin={kin} kout={kout}", flush=True)
+    s, b, pl, ws, o_ws = setup(w, 1, B)
+    stride = kout * kin
+    w_home = synth.expert_weights(w.E, stride * 2, 1).view(np.uint16)
+    pool = synth.expert_weights(w.R * B, stride * 2, 2).view(np.uint16)
+    x = synth.normal_bf16(1, synth.TAG_X, w.NK * kin).reshape(w.NK, kin)
+    y = run_gemm(s, b, ws, B, kin, kout, x, w_home, pool, stride, 0)
+    want = oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, o_ws, kin, kout, x, w_home, pool, stride, 0)
+    A = abs_products(w, pl, o_ws, np.arange(w.NK), x, w_home, pool, 0, kin, kout)
+    exact = check_bound(bits(y), want, A, kin)
+    print(f"[{w.name}] equal to the oracle: {exact:.4f}")
+
+
+def full_size(w, kin, kout, off, seed, nsample):
+    """The dispatch buffer of the workload times its experts' weights (rows of
+    gate, up, down: 3 * H * F bf16), checked on sampled rows."""
+    B = w.E // w.R
+    s, b, pl, ws, o_ws = setup(w, seed, B)
+    H, F = w.H, kout if off == 0 else kin
+    stride = 3 * H * F
+    rng = np.random.default_rng(seed)
+    w_home_np = synth.expert_weights(w.E, stride * 2, seed).view(np.uint16)
+    d_home = to_dev(w_home_np.view(np.int16))
+    pool = torch.empty((w.R * B, stride), dtype=torch.int16, device="cuda")
+    mx.moonep_prefetch_weights(s, b.plan, ws, B, stride * 2, d_home, pool)
+    if kin == H:
+        mx.moonep_dispatch(s, bf16_dev(synth.activations(w, seed)), b.slot_of, b.buf)
+        xin = b.buf
+    else:
+        xin = bf16_dev(synth.normal_bf16(seed, synth.TAG_DY, w.NK * kin).reshape(w.NK, kin))
+    y = torch.empty((w.NK, kout), dtype=torch.bfloat16, device="cuda")
+    y.view(torch.int16).fill_(-1)
+    mx.moonep_expert_gemm(s, b.plan, ws, B, kin, kout, xin, d_home, pool, stride, off, y)
+    torch.cuda.synchronize()
+    assert not (y.view(torch.int16) == -1).all(1).any(), "an output row was not written"
+    rows = np.unique(np.concatenate([rng.integers(0, w.NK, nsample), [0, w.NK - 1],
+                                     np.arange(w.C - 1, w.NK, w.C)]))
+    rows_d = torch.from_numpy(rows).cuda()
+    x_rows = bits(xin[rows_d])
+    pool_np = bits(pool.view(torch.bfloat16))
+    want = oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, o_ws, kin, kout, x_rows, w_home_np, pool_np,
+                              stride, off, rows=rows, x_compact=True)
+    A = abs_products(w, pl, o_ws, rows, x_rows, w_home_np, pool_np, off, kin, kout)
+    exact = check_bound(bits(y[rows_d]), want, A, kin)
+    print(f"[{w.name}] kin={kin} kout={kout} rows={rows.size} equal to the oracle: {exact:.4f}")
+
+
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_gemm_sweep_full_size(proj):
+    w = synth.sweep_workload(4.0, seed=0)
+    F = synth.SWEEP_FFN
+    print(f"[case] sweep maxvio 4 {proj}", flush=True)
+    if proj == "gate":
+        full_size(w, w.H, F, 0, 0, 256)
+    else:
+        full_size(w, F, w.H, 2 * w.H * F, 0, 256)

@@ -864,11 +864,15 @@ def test_expert_gemm_integer_inputs_equal_matmul():
                 Wj = Wp[ws[j]] if ws[j] >= 0 else W[pl.rep_expert[j]]
                 want[r0:r0 + pl.rep_count[j]] = X[r0:r0 + pl.rep_count[j]] @ Wj.T
     np.testing.assert_array_equal(y, bf16_of_f64_exact(want))
-    # listed rows only: same values
+    # listed rows only, with the whole buffer or just those rows as x: same values
     rows = np.array([0, 5, w.NK - 1], dtype=np.int64)
+    Xb = bf16_of_f64_exact(X)
     np.testing.assert_array_equal(
-        oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, ws, kin, kout, bf16_of_f64_exact(X), w_home,
-                           pool, stride, off, rows=rows), y[rows])
+        oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, ws, kin, kout, Xb, w_home, pool, stride, off,
+                           rows=rows), y[rows])
+    np.testing.assert_array_equal(
+        oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, ws, kin, kout, Xb[rows], w_home, pool, stride,
+                           off, rows=rows, x_compact=True), y[rows])
 
 
 def test_expert_gemm_rounds_the_exact_sum_once():
