@@ -10,6 +10,11 @@ dispatch -> combine (identity expert, reading the dispatch buffer in place) -> c
 d_out: the identity expert's backward is the identity) -> replica_grad_reduce
 (expert weight-gradients of 2048 x 1408 fp32).
 
+After the timed steps, a separate timed leg runs the expert compute over the
+dispatch buffer: the grouped GEMM for gate and up (H -> F) and down (F -> H),
+reported as "expert_gemm" with its own roofline against the bf16 MFMA peak
+(2 * rows * H * F flops per projection).
+
 Reported value: dispatch+combine GB/s = algorithmic bytes of the two calls
 divided by their HIP-event time inside the timed steps.  Algorithmic bytes
 per call (what the call must move at least):
@@ -43,6 +48,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak, published
 CALLS = ("route_stats", "plan", "weight_slots", "prefetch", "dispatch", "combine", "combine_bwd",
          "dispatch_bwd", "replica_grad_reduce")
 MOVERS = ("dispatch", "combine", "combine_bwd", "dispatch_bwd")
@@ -153,6 +159,52 @@ def cpu_baseline_sampled(w, seed, ntok=2048):
                       f"bytes / time"}
 
 
+def expert_gemm_leg(mx, s, b, wslot, B_slots, w_home, pool, wbytes, d_out, reps, stream):
+    """Time gate, up (H -> F) and down (F -> H) over the dispatch buffer of the
+    last step's plan; weights are the prefetched [E, 3 H F] bf16 rows."""
+    import torch
+
+    H = s.H
+    F = wbytes // 2 // (3 * H)
+    stride = 3 * H * F
+    wh = w_home.view(torch.bfloat16)
+    pl = pool.view(torch.bfloat16)
+    mid = torch.empty((s.NK, F), dtype=torch.bfloat16, device=b.buf.device)
+    mid2 = torch.empty_like(mid)
+    projs = (("gate", H, F, 0, b.buf, mid), ("up", H, F, H * F, b.buf, mid2),
+             ("down", F, H, 2 * H * F, mid, d_out))
+
+    def run(ev=None):
+        for c, (_, kin, kout, off, xin, yout) in enumerate(projs):
+            if ev is not None:
+                ev[c].record(stream)
+            mx.moonep_expert_gemm(s, b.plan, wslot, B_slots, kin, kout, xin, wh, pl, stride, off,
+                                  yout, stream)
+        if ev is not None:
+            ev[len(projs)].record(stream)
+
+    run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(projs) + 1)]
+           for _ in range(reps)]
+    for i in range(reps):
+        run(evs[i])
+    torch.cuda.synchronize()
+    us = {name: 1e3 * sum(evs[i][c].elapsed_time(evs[i][c + 1]) for i in range(reps)) / reps
+          for c, (name, *_rest) in enumerate(projs)}
+    flops = 2.0 * s.NK * H * F
+    tflops = {k: flops / (v * 1e-6) / 1e12 for k, v in us.items()}
+    total = 3 * flops / (sum(us.values()) * 1e-6) / 1e12
+    del mid, mid2
+    return {"kernel": "expert_gemm_kernel", "rows": s.NK, "H": H, "F": F, "reps": reps,
+            "us": {k: round(v, 1) for k, v in us.items()},
+            "TFLOPs": {k: round(v, 1) for k, v in tflops.items()},
+            "roofline": {"bound": "mfma", "achieved": round(total, 1),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(total / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                         "algorithmic_flops_per_launch": flops}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +213,8 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="sweep", choices=("sweep", "dsv3", "adversarial"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-expert-gemm", action="store_true",
+                    help="skip the timed grouped-GEMM leg after the steps")
     ap.add_argument("--no-copy-probe", action="store_true",
                     help="skip the untimed 1 GiB copy used to calibrate HBM counters")
     args = ap.parse_args()
@@ -371,6 +425,9 @@ def main():
                                             zip(levels, reps_per_level, pref_per_level)}},
         "roofline": roof,
     }
+    if not args.no_expert_gemm:
+        result["expert_gemm"] = expert_gemm_leg(mx, s, b, wslot, B_slots, w_home, pool, wbytes,
+                                                d_out, max(1, min(args.steps, 20)), stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = (cpu_baseline(synth.SWEEP_LEVELS, args.seed)
                                   if args.workload == "sweep"

@@ -35,20 +35,34 @@ namespace moonep {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN, int BK, int S>
 struct GemmCfg {
-    static constexpr int kBK = 64;                  // k per LDS stage
-    static constexpr int kWM = BM / 64, kWN = BN / 64;
+    static constexpr int kBK = BK;                      // k per LDS stage (32 or 64)
+    static constexpr int kStages = S;                   // LDS ring depth; S - 1 stages in flight
+    static constexpr int kCpr = BK / 8;                 // 16-byte chunks per row
+    static constexpr int kRpi = 64 / kCpr;              // rows per LDS-DMA load (1 KiB)
+    static constexpr int kTM = WM / 32, kTN = WN / 32;  // 32 x 32 MFMA tiles per wave
+    static constexpr int kWM = BM / WM, kWN = BN / WN;
     static constexpr int kWavesG = kWM * kWN;
     static constexpr int kThreads = kWavesG * 64;
-    static constexpr int kLdk = kBK + 8;            // padded LDS row, elements
-    static constexpr int kStage = (BM + BN) * kLdk; // elements per stage
-    static constexpr int kAVec = BM * 8 / kThreads; // 16-byte loads per thread
-    static constexpr int kBVec = BN * 8 / kThreads;
-    static constexpr int kLdo = BN + 8;             // epilogue LDS row, elements
-    static constexpr int kOVec = BM * BN / 8 / kThreads;
-    static_assert(BM * (BN + 8) <= 2 * kStage, "epilogue must fit the stages");
-    static_assert(kAVec >= 1 && kBVec >= 1 && kOVec >= 1, "tile too small for the block");
+    static constexpr int kRowBytes = BK * 2;
+    static constexpr int kStageBytes = (BM + BN) * kRowBytes;
+    static constexpr int kAInstr = BM / kRpi / kWavesG; // LDS-DMA loads per wave per stage
+    static constexpr int kBInstr = BN / kRpi / kWavesG;
+    static constexpr int kPerStage = kAInstr + kBInstr;
+    static constexpr int kLdo = BN + 8;                 // epilogue LDS row, elements
+    static constexpr int kOVec = WM * BN / 8 / kThreads;  // 16-byte stores per thread per band
+    static_assert(BK == 32 || BK == 64, "stage depth");
+    static_assert(S >= 2 && (S - 2) * kPerStage <= 63, "outstanding loads must fit vmcnt");
+    static_assert(WM * kLdo * 2 <= S * kStageBytes, "an epilogue band must fit the ring");
+    static_assert(kAInstr >= 1 && kBInstr >= 1 && kOVec >= 1, "tile too small for the block");
+    static_assert(BM % (kRpi * kWavesG) == 0 && BN % (kRpi * kWavesG) == 0, "rows per DMA round");
+    // chunk position of chunk c in row r: c ^ swz(r).  Rows of 128 bytes
+    // (BK = 64) pair up in the 64 banks of 4 bytes, so swz takes row bits
+    // 1..3: the fragment reads of 16 consecutive rows, which the LDS serves
+    // together, land on 16 different 16-byte bank groups.  For 64-byte rows
+    // (BK = 32) four rows share the banks and swz takes row bits 2..3.
+    __device__ static constexpr int swz(int r) { return (r / (16 / kCpr)) % kCpr; }
 };
 
 // Exclusive scan of one int per thread over a block of NW waves.
@@ -89,13 +103,14 @@ struct GemmArgs {
     uint16_t *y;
 };
 
-template <int BM, int BN>
-__global__ __launch_bounds__((GemmCfg<BM, BN>::kThreads)) void expert_gemm_kernel(GemmArgs a)
+template <int BM, int BN, int WM, int WN, int BK, int S>
+__global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, BK, S>::kThreads)) void expert_gemm_kernel(
+    GemmArgs a)
 {
-    using G = GemmCfg<BM, BN>;
+    using G = GemmCfg<BM, BN, WM, WN, BK, S>;
     extern __shared__ __align__(16) uint16_t lds[];
     uint16_t *stage0 = lds;
-    int32_t *seg_start = (int32_t *)(lds + 2 * G::kStage);  // [E + cap + 1]
+    int32_t *seg_start = (int32_t *)((char *)lds + S * G::kStageBytes);  // [E + cap + 1]
     __shared__ int scan_tmp[G::kWavesG];
 
     const int tid = (int)threadIdx.x, lane = lane_id(), wave = tid >> 6;
@@ -137,7 +152,7 @@ __global__ __launch_bounds__((GemmCfg<BM, BN>::kThreads)) void expert_gemm_kerne
     __syncthreads();
 
     // ---- items of this workgroup's XCD -------------------------------------
-    const int32_t nbn = a.out_dim / BN;
+    const int32_t nbn = (a.out_dim + BN - 1) / BN;  // the last block may be part-empty
     const int64_t items = (int64_t)total_tiles * nbn;
     const int xcd = (int)(blockIdx.x % 8), q = (int)(blockIdx.x / 8);
     const int gx = ((int)gridDim.x - xcd + 7) / 8;
@@ -182,136 +197,194 @@ __global__ __launch_bounds__((GemmCfg<BM, BN>::kThreads)) void expert_gemm_kerne
         const int32_t mrows = len - mt * BM < BM ? len - mt * BM : BM;
         const int64_t n0 = (int64_t)nb * BN;
 
-        // global -> register loads of one k stage
-        u32x4 ra[G::kAVec], rb[G::kBVec];
-        auto load = [&](int32_t kt) {
-            const int64_t k0 = (int64_t)kt * G::kBK;
+        // LDS layout of a stage: A rows then B rows, BK bf16 (2 BK bytes) each,
+        // 16-byte chunk c of row r stored at chunk position c ^ swz(r).  One
+        // LDS-DMA load per wave fills kRpi rows (1 KiB, lane i -> byte 16 i):
+        // lane i brings chunk (i % kCpr) ^ swz(r) of row r = kRpi g + i / kCpr.
+        const int dma_row = lane / G::kCpr, dma_pos = lane % G::kCpr;
+        uint32_t a_off[G::kAInstr], b_off[G::kBInstr];
 #pragma unroll
-            for (int v = 0; v < G::kAVec; ++v) {
-                const int idx = tid + v * G::kThreads;
-                const int row = idx >> 3, c = idx & 7;
-                const int64_t gr = m0 + (row < mrows ? row : 0);
-                ra[v] = *(const u32x4 *)(a.x + gr * a.in_dim + k0 + c * 8);
-            }
+        for (int v = 0; v < G::kAInstr; ++v) {
+            const int row = (v * G::kWavesG + wave) * G::kRpi + dma_row;
+            const int chunk = dma_pos ^ G::swz(row);
+            a_off[v] = (uint32_t)((row < mrows ? row : 0) * a.in_dim * 2 + chunk * 16);
+        }
 #pragma unroll
-            for (int v = 0; v < G::kBVec; ++v) {
-                const int idx = tid + v * G::kThreads;
-                const int row = idx >> 3, c = idx & 7;
-                rb[v] = *(const u32x4 *)(wbase + (n0 + row) * a.in_dim + k0 + c * 8);
-            }
+        for (int v = 0; v < G::kBInstr; ++v) {
+            const int row = (v * G::kWavesG + wave) * G::kRpi + dma_row;
+            const int chunk = dma_pos ^ G::swz(row);
+            b_off[v] = (uint32_t)((n0 + row < a.out_dim ? row : 0) * a.in_dim * 2 + chunk * 16);
+        }
+        const char *a_base = (const char *)(a.x + m0 * a.in_dim);
+        const char *b_base = (const char *)(wbase + n0 * a.in_dim);
+        char *lds_b = (char *)stage0;
+        auto issue = [&](int32_t kt, int st) {
+            char *dst = lds_b + st * G::kStageBytes + wave * 1024;
+            const char *ap = a_base + (int64_t)kt * G::kRowBytes;
+            const char *bp = b_base + (int64_t)kt * G::kRowBytes;
+#pragma unroll
+            for (int v = 0; v < G::kAInstr; ++v)
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(ap + a_off[v]),
+                    (__attribute__((address_space(3))) void *)(dst + v * G::kWavesG * 1024), 16, 0, 0);
+#pragma unroll
+            for (int v = 0; v < G::kBInstr; ++v)
+                __builtin_amdgcn_global_load_lds(
+                    (const void *)(bp + b_off[v]),
+                    (__attribute__((address_space(3))) void *)(dst + BM * G::kRowBytes +
+                                                               v * G::kWavesG * 1024),
+                    16, 0, 0);
         };
-        auto store = [&](uint16_t *st) {
-#pragma unroll
-            for (int v = 0; v < G::kAVec; ++v) {
-                const int idx = tid + v * G::kThreads;
-                *(u32x4 *)(st + (idx >> 3) * G::kLdk + (idx & 7) * 8) = ra[v];
-            }
-            uint16_t *sb = st + BM * G::kLdk;
-#pragma unroll
-            for (int v = 0; v < G::kBVec; ++v) {
-                const int idx = tid + v * G::kThreads;
-                *(u32x4 *)(sb + (idx >> 3) * G::kLdk + (idx & 7) * 8) = rb[v];
-            }
+        // fragment of 32 rows from row0 (a multiple of 32) at k-step ks: lane l
+        // reads row row0 + l % 32, chunk 2 ks + l / 32
+        const int fr = lane & 31, fsw = G::swz(lane & 31), fhalf = lane >> 5;
+        auto frag = [&](const char *base, int row0, int ks) -> bf16x8 {
+            return *(const bf16x8 *)(base + (row0 + fr) * G::kRowBytes +
+                                     (((2 * ks + fhalf) ^ fsw) << 4));
         };
 
-        f32x16 acc[2][2];
+        f32x16 acc[G::kTM][G::kTN];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < G::kTM; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int j = 0; j < G::kTN; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     acc[i][j][r] = 0.0f;
 
-        load(0);
-        store(stage0);
-        __syncthreads();
+        // ring of S stages, S - 1 in flight: stage kt lives in slot kt % S
+#pragma unroll
+        for (int st = 0; st + 1 < S; ++st)
+            if (st < nk)
+                issue(st, st);
         for (int32_t kt = 0; kt < nk; ++kt) {
-            if (kt + 1 < nk)
-                load(kt + 1);
-            const uint16_t *sa = stage0 + (kt & 1) * G::kStage;
-            const uint16_t *sb = sa + BM * G::kLdk;
+            // this wave's loads of stage kt have landed once at most the later
+            // stages' loads are outstanding
+            if (kt + S - 2 < nk) {
+                if constexpr (S == 2)
+                    __builtin_amdgcn_s_waitcnt(0x0F70);
+                else if constexpr (S == 3)
+                    __builtin_amdgcn_s_waitcnt(0x0F70 | (G::kPerStage & 15) |
+                                               ((G::kPerStage >> 4) << 14));
+                else
+                    __builtin_amdgcn_s_waitcnt(0x0F70 | ((2 * G::kPerStage) & 15) |
+                                               (((2 * G::kPerStage) >> 4) << 14));
+            } else {
+                __builtin_amdgcn_s_waitcnt(0x0F70);
+            }
+            __syncthreads();  // every wave's part of stage kt is visible; slot (kt-1) % S is free
+            if (kt + S - 1 < nk)
+                issue(kt + S - 1, (kt + S - 1) % S);
+            const char *sa = lds_b + (kt % S) * G::kStageBytes;
+            const char *sb = sa + BM * G::kRowBytes;
+            bf16x8 fa[2][G::kTM], fb[2][G::kTN];
+#pragma unroll
+            for (int i = 0; i < G::kTM; ++i)
+                fa[0][i] = frag(sa, wm * WM + i * 32, 0);
+#pragma unroll
+            for (int j = 0; j < G::kTN; ++j)
+                fb[0][j] = frag(sb, wn * WN + j * 32, 0);
 #pragma unroll
             for (int ks = 0; ks < G::kBK / 16; ++ks) {
-                const int kof = ks * 16 + (lane >> 5) * 8;
-                bf16x8 fa[2], fb[2];
+                const int cur = ks & 1, nxt = cur ^ 1;
+                if (ks + 1 < G::kBK / 16) {
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    fa[i] = *(const bf16x8 *)(sa + (wm * 64 + i * 32 + (lane & 31)) * G::kLdk + kof);
+                    for (int i = 0; i < G::kTM; ++i)
+                        fa[nxt][i] = frag(sa, wm * WM + i * 32, ks + 1);
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    fb[j] = *(const bf16x8 *)(sb + (wn * 64 + j * 32 + (lane & 31)) * G::kLdk + kof);
+                    for (int j = 0; j < G::kTN; ++j)
+                        fb[nxt][j] = frag(sb, wn * WN + j * 32, ks + 1);
+                }
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
+                for (int i = 0; i < G::kTM; ++i)
 #pragma unroll
-                    for (int j = 0; j < 2; ++j)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
-                                                                            0, 0, 0);
+                    for (int j = 0; j < G::kTN; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[cur][i], fb[cur][j],
+                                                                            acc[i][j], 0, 0, 0);
             }
-            if (kt + 1 < nk)
-                store(stage0 + ((kt + 1) & 1) * G::kStage);
-            __syncthreads();
+            // Schedule: the first k-step's fragments, then each later k-step's
+            // fragment reads spread between the MFMAs of the step before, so LDS
+            // latency hides under the matrix work.
+            constexpr int kFr = G::kTM + G::kTN, kMf = G::kTM * G::kTN;
+            __builtin_amdgcn_sched_group_barrier(0x100, kFr, 0);
+#pragma unroll
+            for (int ks = 0; ks + 1 < G::kBK / 16; ++ks) {
+#pragma unroll
+                for (int r = 0; r < kFr; ++r) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, kMf / kFr, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                }
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
         }
+        __syncthreads();  // every wave is done with the ring before the epilogue reuses it
 
-        // ---- epilogue: bf16 tile through LDS, 16-byte row stores -------------
+        // ---- epilogue: one band of wave rows at a time through LDS ------------
         uint16_t *so = stage0;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int band = 0; band < G::kWM; ++band) {
+            if (wm == band) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+                for (int i = 0; i < G::kTM; ++i)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
-                    const int row = wm * 64 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-                    const int col = wn * 64 + j * 32 + (lane & 31);
-                    const uint32_t p = pack_bf16(acc[i][j][r], acc[i][j][r + 1]);
-                    so[row * G::kLdo + col] = (uint16_t)(p & 0xFFFFu);
-                    so[(row + 1) * G::kLdo + col] = (uint16_t)(p >> 16);
-                }
-        __syncthreads();
+                    for (int j = 0; j < G::kTN; ++j)
 #pragma unroll
-        for (int v = 0; v < G::kOVec; ++v) {
-            const int idx = tid + v * G::kThreads;
-            const int row = idx / (BN / 8), c = idx % (BN / 8);
-            if (row < mrows)
-                *(u32x4 *)(a.y + (m0 + row) * a.out_dim + n0 + c * 8) =
-                    *(const u32x4 *)(so + row * G::kLdo + c * 8);
+                        for (int r = 0; r < 16; r += 2) {
+                            const int row = i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+                            const int col = wn * WN + j * 32 + (lane & 31);
+                            const uint32_t p = pack_bf16(acc[i][j][r], acc[i][j][r + 1]);
+                            so[row * G::kLdo + col] = (uint16_t)(p & 0xFFFFu);
+                            so[(row + 1) * G::kLdo + col] = (uint16_t)(p >> 16);
+                        }
+            }
+            __syncthreads();
+#pragma unroll
+            for (int v = 0; v < G::kOVec; ++v) {
+                const int idx = tid + v * G::kThreads;
+                const int row = idx / (BN / 8), c = idx % (BN / 8);
+                const int grow = band * WM + row;
+                if (grow < mrows && n0 + c * 8 < a.out_dim)
+                    *(u32x4 *)(a.y + (m0 + grow) * a.out_dim + n0 + c * 8) =
+                        *(const u32x4 *)(so + row * G::kLdo + c * 8);
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
 }
 
 namespace {
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN, int BK, int S>
 int run_gemm(const GemmArgs &ga, hipStream_t st)
 {
-    using G = GemmCfg<BM, BN>;
-    const size_t lds = (size_t)2 * G::kStage * 2 + (size_t)(ga.E + ga.pl.cap + 1) * 4;
+    using G = GemmCfg<BM, BN, WM, WN, BK, S>;
+    const size_t lds = (size_t)S * G::kStageBytes + (size_t)(ga.E + ga.pl.cap + 1) * 4;
     int dev = 0, cus = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return MOONEP_ERR_HIP;
     static bool raised[64] = {};
     if (dev >= 0 && dev < 64 && !raised[dev]) {
-        if (hipFuncSetAttribute((const void *)expert_gemm_kernel<BM, BN>,
+        if (hipFuncSetAttribute((const void *)expert_gemm_kernel<BM, BN, WM, WN, BK, S>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
             return MOONEP_ERR_HIP;
         raised[dev] = true;
     }
     int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (expert_gemm_kernel<BM, BN>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (expert_gemm_kernel<BM, BN, WM, WN, BK, S>),
                                                      G::kThreads, lds) != hipSuccess)
         return MOONEP_ERR_HIP;
     const int grid = cus * (per_cu > 0 ? per_cu : 1);
-    hipLaunchKernelGGL((expert_gemm_kernel<BM, BN>), dim3(grid), dim3(G::kThreads), lds, st, ga);
+    hipLaunchKernelGGL((expert_gemm_kernel<BM, BN, WM, WN, BK, S>), dim3(grid), dim3(G::kThreads), lds, st, ga);
     return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
 }
 
 }  // namespace
 
-constexpr int kGemmBM = 128, kGemmBN = 128;
+constexpr int kGemmBM = 256, kGemmBN = 256, kGemmWM = 128, kGemmWN = 64, kGemmBK = 64,
+              kGemmStages = 2;
 
-int gemm_out_align() { return kGemmBN; }
+int gemm_out_align() { return 128; }
 
 int launch_expert_gemm(const moonep_shape &s, const int32_t *plan, const int32_t *wslot, int32_t B,
                        int32_t in_dim, int32_t out_dim, const uint16_t *x, const uint16_t *w_home,
@@ -337,7 +410,7 @@ int launch_expert_gemm(const moonep_shape &s, const int32_t *plan, const int32_t
     ga.w_stride = w_stride;
     ga.w_offset = w_offset;
     ga.y = y;
-    return run_gemm<kGemmBM, kGemmBN>(ga, st);
+    return run_gemm<kGemmBM, kGemmBN, kGemmWM, kGemmWN, kGemmBK, kGemmStages>(ga, st);
 }
 
 }  // namespace moonep

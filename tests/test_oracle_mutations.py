@@ -52,8 +52,8 @@ MUTANTS = {
                                        "            if (p->rep_host[j] != d && ++b)\n                continue;"),
     "prefetch_wrong_source": ("w_home + (int64_t)p->rep_expert[j] * wbytes", "w_home + (int64_t)p->rep_host[j] * wbytes"),
     "gemm_ignores_wslot": ("w = wslot[j] >= 0 ? pool", "w = wslot[j] < -1 ? pool"),
-    "gemm_transposed_weight": ("acc += orc_bf16_to_double(x[r * in_dim + k]) * orc_bf16_to_double(wn[k]);",
-                               "acc += orc_bf16_to_double(x[r * in_dim + k]) * orc_bf16_to_double(w[w_offset + (int64_t)k * out_dim + n]);"),
+    "gemm_transposed_weight": ("acc += orc_bf16_to_double(xr[k]) * orc_bf16_to_double(wn[k]);",
+                               "acc += orc_bf16_to_double(xr[k]) * orc_bf16_to_double(w[w_offset + (int64_t)k * out_dim + n]);"),
     "gemm_ignores_offset": ("const uint16_t *wn = w + w_offset + (int64_t)n * in_dim;",
                             "const uint16_t *wn = w + (int64_t)n * in_dim;"),
     "gemm_drops_last_k": ("for (int32_t k = 0; k < in_dim; ++k)\n                    acc",
