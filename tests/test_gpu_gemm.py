@@ -132,13 +132,14 @@ def test_gemm_real_inputs_within_bound(case):
     print(f"[{w.name}] equal to the oracle: {exact:.4f}")
 
 
-def full_size(w, kin, kout, off, seed, nsample):
+def full_size(w, kin, kout, off, seed, nsample, single=False):
     """The dispatch buffer of the workload times its experts' weights (rows of
-    gate, up, down: 3 * H * F bf16), checked on sampled rows."""
+    gate, up, down: 3 * H * F bf16, or one projection if single), checked on
+    sampled rows."""
     B = w.E // w.R
     s, b, pl, ws, o_ws = setup(w, seed, B)
     H, F = w.H, kout if off == 0 else kin
-    stride = 3 * H * F
+    stride = kin * kout if single else 3 * H * F
     rng = np.random.default_rng(seed)
     w_home_np = synth.expert_weights(w.E, stride * 2, seed).view(np.uint16)
     d_home = to_dev(w_home_np.view(np.int16))
@@ -175,3 +176,12 @@ def test_gemm_sweep_full_size(proj):
         full_size(w, w.H, F, 0, 0, 256)
     else:
         full_size(w, F, w.H, 2 * w.H * F, 0, 256)
+
+
+def test_gemm_dsv3_full_size():
+    """DeepSeek-V3-like shape, gate projection 7168 -> 2048 over the 1M-row
+    dispatch buffer (training B = E/R slots, one overflow replica); sampled
+    rows against the oracle."""
+    w = synth.WORKLOADS["dsv3"]
+    print(f"[case] {w.name} gate", flush=True)
+    full_size(w, w.H, 2048, 0, 0, 96, single=True)
