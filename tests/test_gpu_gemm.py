@@ -89,6 +89,7 @@ def check_bound(y_rows, o_rows, A, kin):
 
 SMALL = [
     (synth.WORKLOADS["tiny"], 128, 256),
+    (synth.Workload("max_R_max_E", 512, 1024, 8, 2, 16, "zipf", alpha=1.2), 64, 128),
     (synth.Workload("skew", 4, 16, 100, 4, 64, "zipf", alpha=2.5), 64, 128),
     (synth.Workload("many_ranks", 16, 32, 64, 2, 64, "zipf", alpha=1.3), 192, 384),
     (synth.Workload("one_rank", 1, 4, 50, 2, 64, "zipf", alpha=1.0), 64, 128),

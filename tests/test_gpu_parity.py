@@ -144,6 +144,8 @@ def test_edge_shapes(w):
 
 
 def test_empty_input():
+    """S = 0: every entry point accepts the empty step and writes nothing it
+    should not (the replica reduction and the prefetch have no replica)."""
     w = synth.Workload("empty", 2, 8, 0, 2, 64, "zipf", G=16)
     s = shape_of(w)
     b = mx.allocate(s)
@@ -152,12 +154,42 @@ def test_empty_input():
     b.maxvio.fill_(3.0)
     mx.plan_step(b, e)
     x = torch.empty((0, w.H), dtype=torch.bfloat16, device="cuda")
+    g0 = torch.empty(0, device="cuda")
     mx.moonep_dispatch(s, x, b.slot_of, b.buf)
-    mx.moonep_combine(s, b.buf, torch.empty(0, device="cuda"), b.slot_of, x)
+    mx.moonep_combine(s, b.buf, g0, b.slot_of, x)
+    mx.moonep_combine_bwd(s, x, b.buf, g0, b.slot_of, b.buf.clone(), g0.clone())
+    mx.moonep_dispatch_bwd(s, b.buf, b.slot_of, x.clone())
+    home = torch.full((w.E, w.G), 1.5, device="cuda")
+    rep = torch.full((w.E + w.R, w.G), 2.5, device="cuda")
+    mx.moonep_replica_grad_reduce(s, b.plan, w.G, home, rep)
+    ws = torch.full((w.E + w.R,), 9, dtype=torch.int32, device="cuda")
+    mx.moonep_weight_slots(s, b.plan, 2, ws)
+    wh = torch.ones((w.E, 128 * 64), dtype=torch.bfloat16, device="cuda")
+    pool = torch.full((w.R * 2, 128 * 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    mx.moonep_prefetch_weights(s, b.plan, ws, 2, 128 * 64 * 2, wh, pool)
+    mx.moonep_expert_gemm(s, b.plan, ws, 2, 64, 128, x, wh, pool, 128 * 64, 0,
+                          torch.empty((0, 128), dtype=torch.bfloat16, device="cuda"))
     torch.cuda.synchronize()
+    assert mx.moonep_read_error(b.workspace) == mx.DEV_OK
     assert (b.expert_counts.cpu() == 0).all() and b.maxvio.item() == 0.0
     f = b.plan_fields()
     assert f["n_rep"] == 0 and (f["keep"] == 0).all()
+    assert (home.cpu() == 1.5).all() and (rep.cpu() == 2.5).all()
+    assert (ws.cpu() == -1).all() and (pool.float().cpu() == 3.0).all()
+
+
+LIMITS = [
+    # the largest E and R the plan tables hold (E = 1024, R = 512)
+    synth.Workload("max_R_max_E", 512, 1024, 8, 2, 16, "zipf", alpha=1.2, G=16),
+    synth.Workload("max_E_two_ranks", 2, 1024, 512, 8, 64, "zipf", alpha=1.0, G=24),
+    synth.Workload("max_R_one_hot", 512, 512, 16, 4, 8, "fixed", gates="uniform", G=8),
+]
+
+
+@pytest.mark.parametrize("w", LIMITS, ids=lambda w: w.name)
+def test_shape_limits(w):
+    r = run_and_compare(w, 0)
+    assert r["n_rep"] > 0
 
 
 def test_bad_expert_id_sets_error_word_and_stays_in_bounds():

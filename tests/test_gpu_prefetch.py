@@ -47,6 +47,7 @@ def run_prefetch(w, seed, Bs, wbytes, topk=None):
 
 SMALL = [
     synth.WORKLOADS["tiny"],
+    synth.Workload("max_R_max_E", 512, 1024, 8, 2, 16, "zipf", alpha=1.2),
     synth.Workload("skew", 4, 16, 100, 4, 64, "zipf", alpha=2.5),
     synth.Workload("many_ranks", 16, 32, 64, 2, 64, "zipf", alpha=1.3),
     synth.Workload("one_rank", 1, 4, 50, 2, 64, "zipf", alpha=1.0),
