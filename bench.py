@@ -161,6 +161,31 @@ def cpu_baseline_sampled(w, seed, ntok=2048):
                       f"bytes / time"}
 
 
+def plan_latency(mx, s, b, topks, levels, stream, reps=20):
+    """Median HIP-event time of route_stats + plan per routing level, over
+    `reps` back-to-back pairs on the launching stream (after the timed steps)."""
+    import torch
+
+    out = {}
+    for lv, tk in zip(levels, topks):
+        def pair():
+            mx.moonep_route_stats(s, tk, b.expert_counts, b.maxvio, b.workspace, stream)
+            mx.moonep_plan(s, tk, b.expert_counts, b.workspace, b.plan, b.slot_of, b.src_of_slot,
+                           stream)
+        for _ in range(3):
+            pair()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            pair()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        out[lv] = round(1e3 * t[reps // 2], 2)
+    return out
+
+
 def gemm_traffic(workload):
     """HBM bytes per launch of the GEMM from the committed counter summary, while
     the GEMM sources still hash as they did when the counters were taken."""
@@ -183,6 +208,9 @@ def expert_gemm_leg(mx, s, b, wslot, B_slots, w_home, pool, wbytes, d_out, reps,
     H = s.H
     F = wbytes // 2 // (3 * H)
     stride = 3 * H * F
+    # slots and pool for the plan now in b.plan (untimed)
+    mx.moonep_weight_slots(s, b.plan, B_slots, wslot, stream)
+    mx.moonep_prefetch_weights(s, b.plan, wslot, B_slots, wbytes, w_home, pool, stream)
     wh = w_home.view(torch.bfloat16)
     pl = pool.view(torch.bfloat16)
     mid = torch.empty((s.NK, F), dtype=torch.bfloat16, device=b.buf.device)
@@ -373,9 +401,10 @@ def main():
     dc_bytes = byt["dispatch"] + byt["combine"]
     dc_s = 1e-3 * (mean(per_call["dispatch"]) + mean(per_call["combine"]))
     value = dc_bytes / dc_s / 1e9
-    plan_us = {lv: round(1e3 * (mean(per_level[lv]["route_stats"]) +
-                                      mean(per_level[lv]["plan"])), 2)
-               for lv in levels if per_level[lv]["plan"]}
+    plan_us_in_step = {lv: round(1e3 * (mean(per_level[lv]["route_stats"]) +
+                                        mean(per_level[lv]["plan"])), 2)
+                       for lv in levels if per_level[lv]["plan"]}
+    plan_us = plan_latency(mx, s, b, topks, levels, stream)
     pv = list(plan_us.values())
     kern = {}
     for name in MOVERS + ("replica_grad_reduce", "prefetch"):
@@ -432,6 +461,8 @@ def main():
                                                         "combine"))), 0),
         "plan_us_vs_maxvio": plan_us,
         "plan_spread": round((max(pv) - min(pv)) / min(pv), 4) if pv else None,
+        "plan_def": "route_stats + plan, median of 20 back-to-back pairs per level, HIP events",
+        "plan_us_in_step": plan_us_in_step,
         "breakdown_us": us,
         "kernels": kern,
         "replicas_per_level": {lv: int(sum(r)) for lv, r in zip(levels, reps_per_level)},

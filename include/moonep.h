@@ -20,6 +20,13 @@
  * The R ranks are logical: rank r's [C, H] bf16 buffer is rows [r*C, (r+1)*C)
  * of one device allocation.
  *
+ * A step.  Forward: moonep_route_stats, moonep_plan, moonep_weight_slots and
+ * moonep_prefetch_weights (the replicas' weights), moonep_dispatch, the expert
+ * computation over the buffer (moonep_expert_gemm per projection, with the
+ * caller's activation between projections), moonep_combine.  Backward:
+ * moonep_combine_bwd, the expert's backward (the caller's), moonep_dispatch_bwd,
+ * and moonep_replica_grad_reduce for the replicas' weight-gradients.
+ *
  * Conventions shared by every call:
  *  - All array arguments are DEVICE pointers owned by the caller; the library
  *    allocates nothing and keeps no state between calls.

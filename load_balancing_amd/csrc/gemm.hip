@@ -15,14 +15,19 @@
 // host).  Segments are cut into tiles of BM rows that never cross a segment,
 // so every tile multiplies by one weight matrix.
 //
-// Kernel: a persistent grid.  Every workgroup first scans the per-segment tile
-// counts into LDS (n_rep is known only on the device), then walks
-// (tile, column-block) items.  The items of each XCD are one contiguous range,
-// so the workgroups running together on one XCD share their row tile and the
-// segment's weights in that XCD's L2.  Per item: BM x BN outputs, K in steps
-// of 64 through double-buffered, padded LDS tiles; each wave computes 64 x 64
-// with 2 x 2 v_mfma_f32_32x32x16_bf16 accumulators (fp32), then the tile is
-// rounded to bf16 (nearest even) and stored through LDS as 16-byte rows.
+// Kernel: a persistent grid, one workgroup per CU.  Every workgroup first
+// scans the per-segment tile counts into LDS (n_rep is known only on the
+// device), then walks (tile, column-block) items.  The items of each XCD are
+// one contiguous range, so the workgroups running together on one XCD share
+// their row tile and the segment's weights in that XCD's L2.  Per item: BM x BN
+// outputs; K advances BK at a time through a ring of S LDS stages filled by
+// LDS-DMA (global_load_lds_dwordx4: no staging registers), with the 16-byte
+// chunks of each row XOR-swizzled so that fragment reads are free of bank
+// conflicts.  Each wave computes WM x WN outputs with (WM/32) x (WN/32)
+// v_mfma_f32_32x32x16_bf16 accumulators (fp32); scheduling hints interleave
+// the next k-step's fragment reads with the current MFMAs.  The tile is then
+// rounded to bf16 (nearest even) and stored through LDS as 16-byte rows, one
+// band of waves at a time.  The configuration used is at the end of the file.
 //
 // MFMA lane layouts (checked on gfx950): operand A lane l holds row l % 32,
 // k = (l / 32) * 8 .. + 7; operand B lane l holds column l % 32, same k; the

@@ -1,5 +1,6 @@
 // movers.hip -- dispatch (fused permute), combine (fused weighted
-// unpermute) and combine backward over the static expert-grouped buffer.
+// unpermute), combine backward and dispatch backward over the static
+// expert-grouped buffer.
 //
 // The MoonEP article (ncijnetwork.com), three-property list and explainer
 // "pillars" panel: tokens are written straight into their expert-grouped
@@ -8,10 +9,10 @@
 // aipricedb.com README excerpt adds that the copy from the communication
 // buffer into a user buffer is what this removes.
 //
-// All three are HBM-bound streams of 16-byte bf16 vectors (8 per lane); each
+// All four are HBM-bound streams of 16-byte bf16 vectors (8 per lane); each
 // of a token's K rows of the buffer is one contiguous 2H-byte run, so every
-// access is fully coalesced, and token rows are read once.  Combine and its
-// backward give one workgroup to one token: its K destination rows and gates
+// access is fully coalesced, and token rows are read once.  Combine and the
+// two backwards give one workgroup to one token: its K destination rows and gates
 // are uniform (scalar) loads and all K row loads of a thread are issued before
 // any use (out-of-range slots read row 0 and are masked afterwards, so no
 // branch splits the loads).  Dispatch paces its stores instead (see there).
@@ -38,9 +39,10 @@ inline int block_for(int32_t V)
 // Resident waves per CU that measured best on gfx950 for each mover in the
 // full step on the expert-grouped access pattern (HBM efficiency falls when
 // more scattered row requests are in flight; too few leave it idle):
-// dispatch 12, combine 8, combine_bwd 16 -- 3, 2 and 4 workgroups of 256
-// threads.  Uncapped, the same kernels ran 2-4% slower (combine 212 us
-// against 198 us on the 1.2 GB sweep step).
+// dispatch 12, combine 8, combine_bwd 16, dispatch_bwd 12 -- 3, 2, 4 and 3
+// workgroups of 256 threads.  Uncapped, the same kernels ran 2-4% slower
+// (combine 212 us against 198 us on the 1.2 GB sweep step); dispatch_bwd, whose
+// fp64 sums need 154 VGPRs, ran 228 us at 8 waves and 203 us at 12.
 constexpr int kDispatchWaves = 12, kCombineWaves = 8, kCombineBwdWaves = 16,
               kDispatchBwdWaves = 12;
 
