@@ -180,16 +180,22 @@ __device__ void wave_plan(const PlanLds &S, const int32_t *__restrict__ counts, 
         S.dflag[r] = ld < C ? 1 : 0;
     }
     wave_sync();
+    // Everything below does the same work whatever the data: loads use
+    // clamped indices, and a lane with nothing to store writes a spare slot
+    // that no plan uses (index E of an expert array: at least one rank is not
+    // overfull, so at most E - 1 experts spill; index R of a rank array: when
+    // C > 0 at least one rank is not underfull; index cap - 1 of a replica
+    // array: n_rep <= nA + nB - 1 <= cap - 2).  So the plan takes the same
+    // time with or without replicas.
+
     // whole-expert spill of overfull ranks, lowest expert id first
     for (int e = lane; e < E; e += 64) {
         const int32_t r = e / Lx;
         const int32_t excess = S.load[r] - C;
-        int32_t give = 0;
-        if (excess > 0) {
-            const int32_t before = S.P[e] - S.P[r * Lx];
-            give = excess - before;
-            give = give < 0 ? 0 : (give > S.T[e] ? S.T[e] : give);
-        }
+        const int32_t before = S.P[e] - S.P[r * Lx];
+        int32_t give = excess - before;
+        give = give < 0 ? 0 : (give > S.T[e] ? S.T[e] : give);
+        give = excess > 0 ? give : 0;
         S.spill[e] = give;
         S.keep[e] = S.T[e] - give;
         S.sflag[e] = give > 0 ? 1 : 0;
@@ -203,29 +209,25 @@ __device__ void wave_plan(const PlanLds &S, const int32_t *__restrict__ counts, 
     // compact the spill (A) and deficit (B) lists
     for (int e = lane; e < E; e += 64) {
         const int32_t r = e / Lx;
-        if (S.spill[e] > 0) {
-            const int i = S.sidx[e];
-            S.Aval[i] = S.Sp[e] + S.spill[e];
-            S.Aexp[i] = e;
-            S.Aexcl[i] = S.Sp[e];
-        }
+        const int i = S.spill[e] > 0 ? S.sidx[e] : E;
+        S.Aval[i] = S.Sp[e] + S.spill[e];
+        S.Aexp[i] = e;
+        S.Aexcl[i] = S.Sp[e];
         // first destination row of expert e at home: rank base + earlier keeps
         S.home_dst[e] = r * C + (S.P[e] - S.P[r * Lx]) - (S.Sp[e] - S.Sp[r * Lx]);
         S.rep_first[e] = 0;
         S.rep_cnt[e] = 0;
     }
-    for (int r = lane; r < R; r += 64)
-        if (S.D[r] > 0) {
-            const int j = S.didx[r];
-            S.Bval[j] = S.Dp[r] + S.D[r];
-            S.Brank[j] = r;
-            S.Bexcl[j] = S.Dp[r];
-        }
+    for (int r = lane; r < R; r += 64) {
+        const int j = S.D[r] > 0 ? S.didx[r] : R;
+        S.Bval[j] = S.Dp[r] + S.D[r];
+        S.Brank[j] = r;
+        S.Bexcl[j] = S.Dp[r];
+    }
     wave_sync();
 
     // The loops below run over all E (or R) slots with the list length as a
-    // predicate, and the searches have fixed depth: the plan takes the same
-    // time however many experts spill.
+    // predicate, and the searches have fixed depth.
     const int ea = ceil_log2(E + 1), rb = ceil_log2(R + 1);
 
     // deficit totals that coincide with a spill total
@@ -242,67 +244,56 @@ __device__ void wave_plan(const PlanLds &S, const int32_t *__restrict__ counts, 
     for (int i = lane; i < E; i += 64) {
         const bool live = i < nA;
         const int cb = count_below_sorted(S.Bval, nB, live ? S.Aval[i] : 0, rb);
-        if (live) {
-            const int pos = i + S.NC[cb];
-            S.U[pos] = S.Aval[i];
-            S.rai[pos] = i;
-            S.rbj[pos] = cb;
-            S.posA[i] = pos;
-        }
+        const int pos = live ? i + S.NC[cb] : cap - 1;
+        S.U[pos] = S.Aval[i];
+        S.rai[pos] = i;
+        S.rbj[pos] = cb;
+        S.posA[live ? i : E] = pos;
     }
     wave_sync();
     for (int j = lane; j < R; j += 64) {
-        if (j >= nB)
-            continue;
-        int pos;
-        if (S.nc[j]) {
-            pos = S.Bca[j] + S.NC[j];
-            S.U[pos] = S.Bval[j];
-            S.rai[pos] = S.Bca[j];
-            S.rbj[pos] = j;
-        } else {
-            pos = S.posA[S.Bca[j]];
-        }
-        S.posB[j] = pos;
+        const bool live = j < nB;
+        const int ca = S.Bca[j];
+        const bool own = live && S.nc[j];  // a deficit boundary no spill boundary shares
+        const int pos = own ? ca + S.NC[j] : S.posA[ca < E ? ca : E];
+        const int w = own ? pos : cap - 1;
+        S.U[w] = S.Bval[j];
+        S.rai[w] = ca;
+        S.rbj[w] = j;
+        S.posB[live ? j : R] = pos;
     }
     wave_sync();
 
     // replicas, per-expert ranges, header scalars
     for (int m = lane; m < cap; m += 64) {
-        if (m < n_rep) {
-            const int32_t lo = m ? S.U[m - 1] : 0;
-            const int i = S.rai[m], j = S.rbj[m];
-            const int32_t host = S.Brank[j];
-            S.rexp[m] = S.Aexp[i];
-            S.rhost[m] = host;
-            S.rcnt[m] = S.U[m] - lo;
-            S.rso[m] = lo - S.Aexcl[i];
-            S.rrow[m] = S.load[host] + (lo - S.Bexcl[j]);
-            S.rdst[m] = host * C + S.rrow[m] - S.rso[m];
-        } else {
-            S.rexp[m] = 0;
-            S.rhost[m] = 0;
-            S.rcnt[m] = 0;
-            S.rso[m] = 0;
-            S.rrow[m] = 0;
-            S.rdst[m] = 0;
-        }
+        const bool live = m < n_rep;
+        const int32_t lo = m ? S.U[m - 1] : 0;
+        int i = S.rai[m], j = S.rbj[m];  // stale past n_rep: clamp to keep reads in bounds
+        i = i < 0 ? 0 : (i > E ? E : i);
+        j = j < 0 ? 0 : (j > R ? R : j);
+        int32_t host = S.Brank[j];
+        host = host < 0 ? 0 : (host >= R ? R - 1 : host);
+        const int32_t rso = lo - S.Aexcl[i];
+        const int32_t rrow = S.load[host] + (lo - S.Bexcl[j]);
+        S.rexp[m] = live ? S.Aexp[i] : 0;
+        S.rhost[m] = live ? host : 0;
+        S.rcnt[m] = live ? S.U[m] - lo : 0;
+        S.rso[m] = live ? rso : 0;
+        S.rrow[m] = live ? rrow : 0;
+        S.rdst[m] = live ? host * C + rrow - rso : 0;
     }
     for (int i = lane; i < E; i += 64) {
-        if (i >= nA)
-            continue;
-        const int e = S.Aexp[i];
+        int e = S.Aexp[i];
+        e = i < nA && e >= 0 && e < E ? e : E;
         const int f = i ? S.posA[i - 1] + 1 : 0;
         S.rep_first[e] = f;
         S.rep_cnt[e] = S.posA[i] - f + 1;
     }
     int most = 0;
     for (int j = lane; j < R; j += 64) {
-        if (j >= nB)
-            continue;
         const int f = j ? S.posB[j - 1] + 1 : 0;
         const int c = S.posB[j] - f + 1;  // replicas hosted by this rank
-        most = c > most ? c : most;
+        most = j < nB && c > most ? c : most;
     }
     int tmax = 0;
     for (int e = lane; e < E; e += 64)
@@ -422,13 +413,16 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
             const int32_t f = S.rep_first[ee];
             const int32_t last = f + S.rep_cnt[ee] - 1;
             int32_t j = f;
+            // the table reads happen whether or not the entry has a replica, so
+            // the loop costs the same with and without replicas
             for (int st = search_steps; st >= 0; --st) {
                 const int32_t t = j + (1 << st);
                 const int32_t tt = t <= last ? t : last;  // keep the read in the table
-                const bool step = t <= last && S.rso[tt < 0 ? 0 : tt] <= q;
-                j = step ? t : j;
+                const int32_t so = S.rso[tt < 0 ? 0 : tt];
+                j = t <= last && so <= q ? t : j;
             }
-            const int32_t dst = pos < kp ? home : S.rdst[j] + q;
+            const int32_t rd = S.rdst[j < 0 ? 0 : j];
+            const int32_t dst = pos < kp ? home : rd + q;
             // dst is in range whenever counts match topk; the check keeps a
             // mismatched call from writing outside src_of_slot.
             if (ok && (uint64_t)(uint32_t)dst < (uint64_t)nk) {
