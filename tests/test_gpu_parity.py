@@ -286,3 +286,22 @@ def test_plan_random_shapes():
         if N:
             np.testing.assert_array_equal(b.slot_of.cpu().numpy(), slot_of, err_msg=msg)
             np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot, err_msg=msg)
+
+
+def test_whole_chain_random_shapes():
+    """The element-by-element chain (plan, dispatch, combine, both backwards,
+    the reduction) on 40 random shapes: ranks, experts per rank, K up to 9
+    (a second pass of the K loop), ragged token counts, rows of 1 to 257
+    16-byte vectors, and skews from uniform to a few hot experts."""
+    rng = np.random.default_rng(23)
+    for case in range(40):
+        R = int(rng.integers(1, 13))
+        L = int(rng.integers(1, 7))
+        E = R * L
+        K = int(rng.integers(1, min(E, 9) + 1))
+        S = int(rng.integers(1, 70))
+        H = 8 * int(rng.choice([1, 2, 3, 8, 17, 64, 257]))
+        G = int(rng.integers(1, 300))
+        w = synth.Workload(f"rand{case}", R, E, S, K, H, "zipf",
+                           alpha=float(rng.uniform(0.0, 2.5)), G=G)
+        run_and_compare(w, case)
