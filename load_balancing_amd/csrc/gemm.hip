@@ -368,12 +368,16 @@ int run_gemm(const GemmArgs &ga, hipStream_t st)
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         return MOONEP_ERR_HIP;
+    // Raise the kernel's dynamic-LDS limit once per device, to what the largest
+    // allowed E and R need, so later calls with other shapes fit as well.
     static bool raised[64] = {};
-    if (dev >= 0 && dev < 64 && !raised[dev]) {
+    if (dev < 0 || dev >= 64 || !raised[dev]) {
+        const size_t most = (size_t)S * G::kStageBytes + (size_t)(2 * kMaxExperts + kMaxRanks + 1) * 4;
         if (hipFuncSetAttribute((const void *)expert_gemm_kernel<BM, BN, WM, WN, BK, S>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)most) != hipSuccess)
             return MOONEP_ERR_HIP;
-        raised[dev] = true;
+        if (dev >= 0 && dev < 64)
+            raised[dev] = true;
     }
     int per_cu = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (expert_gemm_kernel<BM, BN, WM, WN, BK, S>),

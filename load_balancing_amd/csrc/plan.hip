@@ -448,14 +448,20 @@ int launch_plan(const moonep_shape &s, const int32_t *topk, const int32_t *count
         ++steps;
     const size_t lds = plan_lds_bytes(s.E, s.R);
     if (lds > 65536) {
-        // Large E and R need more than the default 64 KiB of dynamic LDS.
-        static bool raised = false;
-        if (!raised) {
+        // Large E and R need more than the default 64 KiB of dynamic LDS: raise
+        // the kernel's limit once per device, to what the largest allowed shape
+        // needs, so later calls with other shapes fit as well.
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess)
+            return MOONEP_ERR_HIP;
+        static bool raised[64] = {};
+        if (dev < 0 || dev >= 64 || !raised[dev]) {
             if (hipFuncSetAttribute((const void *)plan_slots_kernel,
                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)lds) != hipSuccess)
+                                    (int)plan_lds_bytes(kMaxExperts, kMaxRanks)) != hipSuccess)
                 return MOONEP_ERR_HIP;
-            raised = true;
+            if (dev >= 0 && dev < 64)
+                raised[dev] = true;
         }
     }
     hipLaunchKernelGGL(plan_slots_kernel, dim3(blocks), dim3(kBlock), lds, st, topk, counts, base,
