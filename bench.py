@@ -16,7 +16,11 @@ reported as "expert_gemm" with its own roofline against the bf16 MFMA peak
 (2 * rows * H * F flops per projection).
 
 Reported value: dispatch+combine GB/s = algorithmic bytes of the two calls
-divided by their HIP-event time inside the timed steps.  Algorithmic bytes
+divided by their HIP-event time inside the timed steps.  Before each of the
+four movers an untimed 512 MiB read evicts the 256 MB MALL and the L2, so no
+mover reads what the call before it left in cache (combine, reading the rows
+dispatch has just written, ran ~6% faster without it).  A read, not a write:
+a write would leave dirty lines for the timed call to write back.  Algorithmic bytes
 per call (what the call must move at least):
   dispatch    = N*H*2 (read x once) + NK*H*2 (write rows) + NK*4 (slot_of)
   combine     = NK*H*2 (read rows) + N*H*2 (write y) + NK*8 (slot_of, gates)
@@ -267,6 +271,8 @@ def main():
                     help="skip the timed grouped-GEMM leg after the steps")
     ap.add_argument("--no-copy-probe", action="store_true",
                     help="skip the untimed 1 GiB copy used to calibrate HBM counters")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the untimed 512 MiB cache-evicting read before each mover")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark measures one GPU: R logical ranks are slices of one "
@@ -336,6 +342,11 @@ def main():
     d_g = torch.empty(NK, dtype=torch.float32, device=dev)
     dx = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
+    flush_buf = torch.ones(1 << 27, dtype=torch.float32, device=dev)   # 512 MiB
+
+    def flush():
+        if not args.no_flush:
+            flush_buf.sum()
 
     def step(i, ev=None):
         lv = i % len(levels)
@@ -354,11 +365,13 @@ def main():
             lambda: mx.moonep_replica_grad_reduce(s, b.plan, G, home, rep, stream),
         )
         for c, fn in enumerate(calls):
+            if CALLS[c] in MOVERS:
+                flush()
             if ev is not None:
-                ev[c].record(stream)
+                ev[c][0].record(stream)
             fn()
-        if ev is not None:
-            ev[len(calls)].record(stream)
+            if ev is not None:
+                ev[c][1].record(stream)
 
     # replica counts per level (for the reduce's algorithmic bytes) and the
     # replicas given a prefetch slot (for the prefetch's)
@@ -383,8 +396,8 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(CALLS) + 1)]
-              for _ in range(args.steps)]
+    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(len(CALLS))] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -397,7 +410,7 @@ def main():
     for i in range(args.steps):
         lv = levels[i % len(levels)]
         for c, name in enumerate(CALLS):
-            ms = events[i][c].elapsed_time(events[i][c + 1])
+            ms = events[i][c][0].elapsed_time(events[i][c][1])
             per_call[name].append(ms)
             per_level[lv][name].append(ms)
     mean = lambda v: sum(v) / len(v)
@@ -458,6 +471,8 @@ def main():
                    "global_batch": N, "parallelism": f"1 GPU, {R} logical ranks"},
         "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "value_def": "dispatch+combine algorithmic bytes / their HIP-event time",
+        "cache": ("warm: no flush between calls" if args.no_flush else
+                  "cold: untimed 512 MiB read before each mover call evicts MALL and L2"),
         "forward_GBps_incl_plan": round(dc_bytes / (1e-3 * (mean(per_call["dispatch"]) +
                                                             mean(per_call["combine"]) +
                                                             mean(per_call["route_stats"]) +

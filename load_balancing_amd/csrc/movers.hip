@@ -37,13 +37,15 @@ inline int block_for(int32_t V)
 }
 
 // Resident waves per CU that measured best on gfx950 for each mover in the
-// full step on the expert-grouped access pattern (HBM efficiency falls when
-// more scattered row requests are in flight; too few leave it idle):
-// dispatch 12, combine 8, combine_bwd 16, dispatch_bwd 12 -- 3, 2, 4 and 3
-// workgroups of 256 threads.  Uncapped, the same kernels ran 2-4% slower
-// (combine 212 us against 198 us on the 1.2 GB sweep step); dispatch_bwd, whose
-// fp64 sums need 154 VGPRs, ran 228 us at 8 waves and 203 us at 12.
-constexpr int kDispatchWaves = 12, kCombineWaves = 8, kCombineBwdWaves = 16,
+// full step on the expert-grouped access pattern, each call starting with
+// the MALL and L2 evicted (HBM efficiency falls when more scattered row
+// requests are in flight; too few leave it idle): dispatch 12, combine 12,
+// combine_bwd 16, dispatch_bwd 12 -- 3, 3, 4 and 3 workgroups of 256 threads.
+// On the 1.2 GB sweep step: dispatch 225 us at 12 against 231-235 at 8, 16
+// and 20; combine 198 us at 12 against 210 at 8 and 209 at 16; combine_bwd
+// 431 us at 16 against 445 at 12; dispatch_bwd, whose fp64 sums need 154
+// VGPRs, 228 us at 8 and 203 at 12-20.
+constexpr int kDispatchWaves = 12, kCombineWaves = 12, kCombineBwdWaves = 16,
               kDispatchBwdWaves = 12;
 
 // Dynamic LDS a workgroup of `threads` requests so that only
