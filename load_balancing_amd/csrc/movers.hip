@@ -44,9 +44,12 @@ inline int block_for(int32_t V)
 // On the 1.2 GB sweep step: dispatch 225 us at 12 against 231-235 at 8, 16
 // and 20; combine 198 us at 12 against 210 at 8 and 209 at 16; combine_bwd
 // 431 us at 16 against 445 at 12; dispatch_bwd, whose fp64 sums need 154
-// VGPRs, 228 us at 8 and 203 at 12-20.
-constexpr int kDispatchWaves = 12, kCombineWaves = 12, kCombineBwdWaves = 16,
-              kDispatchBwdWaves = 12;
+// VGPRs, 228 us at 8 and 203 at 12-20.  Dispatch of rows longer than one
+// workgroup (workgroups of one column block, H = 4096 and 7168) does best at
+// 16: 1608 us against 1719 at 12 on the adversarial shape, 3183 against 3357
+// on the DeepSeek-V3-like one (8 waves: 2121 and 3900; 20-24: in between).
+constexpr int kDispatchWaves = 12, kDispatchBlocksWaves = 16, kCombineWaves = 12,
+              kCombineBwdWaves = 16, kDispatchBwdWaves = 12;
 
 // Dynamic LDS a workgroup of `threads` requests so that only
 // waves_per_cu / (threads / 64) of them fit in one CU's LDS; the kernels do not
@@ -437,7 +440,7 @@ int launch_dispatch(const moonep_shape &s, const uint16_t *x, const int32_t *slo
     const int32_t ncb = (V + bs - 1) / bs;
     const int64_t total = N * ncb;
     const uint32_t grid = (uint32_t)(total < (1 << 24) ? total : (1 << 24));
-    const size_t lds = residency_lds(kDispatchWaves, bs);
+    const size_t lds = residency_lds(ncb == 1 ? kDispatchWaves : kDispatchBlocksWaves, bs);
     if (ncb == 1)
         hipLaunchKernelGGL(dispatch_kernel, dim3(grid, 1), dim3(bs), lds, st, (const u32x4 *)x,
                            slot_of, (u32x4 *)buf, N, V, s.K, nrows);
