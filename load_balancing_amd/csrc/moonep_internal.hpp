@@ -178,7 +178,23 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 load_nt(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+
+// Three cache policies for 16-byte stores.  Which one a mover uses was
+// measured per kernel on gfx950, each call starting from an evicted cache:
+//   store_nt  -- non-temporal (streaming);
+//   store_wb  -- plain write-back through L2 (dispatch: 208 us against 225
+//                non-temporal on the 1.2 GB sweep step);
+//   store_dev -- device scope (sc1), written through L2 (combine 191 us
+//                against 198, combine_bwd 389 against 432).
+// The scope bits have no builtin for 16-byte stores, hence the asm; the
+// compiler counts no memory operation for it, so its waits can only be
+// longer than needed, never shorter.
 __device__ __forceinline__ void store_nt(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void store_wb(u32x4 *p, u32x4 v) { *p = v; }
+__device__ __forceinline__ void store_dev(u32x4 *p, u32x4 v)
+{
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(p), "v"(v) : "memory");
+}
 
 // Exclusive scan over a block of kBlock threads of one int per thread.
 // `tmp` must hold kWaves ints of LDS.  Returns the exclusive prefix; *total

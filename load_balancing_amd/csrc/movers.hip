@@ -16,8 +16,11 @@
 // are uniform (scalar) loads and all K row loads of a thread are issued before
 // any use (out-of-range slots read row 0 and are masked afterwards, so no
 // branch splits the loads).  Dispatch paces its stores instead (see there).
-// Write-once and read-once streams use non-temporal accesses, which measured
-// faster on gfx950 than cached ones for every mover.
+// Loads are non-temporal, which measured faster on gfx950 than cached ones
+// for every mover.  Stores take the policy that measured fastest per kernel
+// from an evicted cache (see store_nt / store_wb / store_dev): write-back for
+// dispatch, device scope for combine and combine_bwd, non-temporal for
+// dispatch_bwd.
 #include "moonep_internal.hpp"
 
 namespace moonep {
@@ -130,7 +133,7 @@ __device__ __forceinline__ void dispatch_column(const u32x4 *__restrict__ x,
     for (int32_t k = 0; k < K; ++k) {
         const uint32_t sk = (uint32_t)so[k];
         if (sk < nrows)
-            store_nt(buf + (int64_t)sk * V + v, val);
+            store_wb(buf + (int64_t)sk * V + v, val);
     }
 }
 
@@ -237,7 +240,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const u32x4 *__restrict
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 r[j] = pack_bf16(acc[2 * j], acc[2 * j + 1]);
-            store_nt(y + (int64_t)tok * V + v, r);
+            store_dev(y + (int64_t)tok * V + v, r);
         }
     }
 }
@@ -361,12 +364,12 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(
             if (all) {
 #pragma unroll
                 for (int c = 0; c < kN; ++c)
-                    store_nt(d_out + (int64_t)sl.s[c] * V + v, r[c]);
+                    store_dev(d_out + (int64_t)sl.s[c] * V + v, r[c]);
             } else {
 #pragma unroll
                 for (int c = 0; c < kN; ++c)
                     if (sl.s[c] != 0xFFFFFFFFu)
-                        store_nt(d_out + (int64_t)sl.s[c] * V + v, r[c]);
+                        store_dev(d_out + (int64_t)sl.s[c] * V + v, r[c]);
             }
         }
 #pragma unroll
