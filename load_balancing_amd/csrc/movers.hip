@@ -240,7 +240,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const u32x4 *__restrict
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 r[j] = pack_bf16(acc[2 * j], acc[2 * j + 1]);
-            store_dev(y + (int64_t)tok * V + v, r);
+            store_dev(y + (int64_t)tok * V, (uint32_t)V * 16u, (uint32_t)v * 16u, r);
         }
     }
 }
@@ -364,12 +364,12 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(
             if (all) {
 #pragma unroll
                 for (int c = 0; c < kN; ++c)
-                    store_dev(d_out + (int64_t)sl.s[c] * V + v, r[c]);
+                    store_dev(d_out + (int64_t)sl.s[c] * V, (uint32_t)V * 16u, (uint32_t)v * 16u, r[c]);
             } else {
 #pragma unroll
                 for (int c = 0; c < kN; ++c)
                     if (sl.s[c] != 0xFFFFFFFFu)
-                        store_dev(d_out + (int64_t)sl.s[c] * V + v, r[c]);
+                        store_dev(d_out + (int64_t)sl.s[c] * V, (uint32_t)V * 16u, (uint32_t)v * 16u, r[c]);
             }
         }
 #pragma unroll
