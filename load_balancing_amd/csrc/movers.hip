@@ -41,17 +41,18 @@ inline int block_for(int32_t V)
 
 // Resident waves per CU that measured best on gfx950 for each mover in the
 // full step on the expert-grouped access pattern, each call starting with
-// the MALL and L2 evicted (HBM efficiency falls when more scattered row
-// requests are in flight; too few leave it idle): dispatch 12, combine 12,
-// combine_bwd 16, dispatch_bwd 12 -- 3, 3, 4 and 3 workgroups of 256 threads.
-// On the 1.2 GB sweep step: dispatch 225 us at 12 against 231-235 at 8, 16
-// and 20; combine 198 us at 12 against 210 at 8 and 209 at 16; combine_bwd
-// 431 us at 16 against 445 at 12; dispatch_bwd, whose fp64 sums need 154
-// VGPRs, 228 us at 8 and 203 at 12-20.  Dispatch of rows longer than one
-// workgroup (workgroups of one column block, H = 4096 and 7168) does best at
-// 16: 1608 us against 1719 at 12 on the adversarial shape, 3183 against 3357
-// on the DeepSeek-V3-like one (8 waves: 2121 and 3900; 20-24: in between).
-constexpr int kDispatchWaves = 12, kDispatchBlocksWaves = 16, kCombineWaves = 12,
+// the MALL and L2 evicted and with the store policies below (HBM efficiency
+// falls when more scattered row requests are in flight; too few leave it
+// idle): dispatch 16, combine 12, combine_bwd 16, dispatch_bwd 12 -- 4, 3, 4
+// and 3 workgroups of 256 threads.  On the 1.2 GB sweep step: dispatch 199 us
+// at 16 against 207 at 12, 202 at 20 and 230 at 8; combine 190 us at 12
+// against 195 at 16 and 205 at 8; combine_bwd 387 us at 16, the same at 20
+// and 24, 430 at 12; dispatch_bwd, whose fp64 sums need 154 VGPRs, 228 us at
+// 8 and 203 at 12-20.  Rows longer than one workgroup (workgroups of one
+// column block, H = 4096 and 7168) dispatch best at 16 as well: 1608 us
+// against 1719 at 12 on the adversarial shape, 3183 against 3357 on the
+// DeepSeek-V3-like one.
+constexpr int kDispatchWaves = 16, kDispatchBlocksWaves = 16, kCombineWaves = 12,
               kCombineBwdWaves = 16, kDispatchBwdWaves = 12;
 
 // Dynamic LDS a workgroup of `threads` requests so that only
