@@ -178,29 +178,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ u32x4 load_nt(const u32x4 *p) { return __builtin_nontemporal_load(p); }
-
-// Three cache policies for 16-byte stores.  Which one a mover uses was
-// measured per kernel on gfx950, each call starting from an evicted cache:
-//   store_nt  -- non-temporal (streaming);
-//   store_wb  -- plain write-back through L2 (dispatch: 208 us against 225
-//                non-temporal on the 1.2 GB sweep step);
-//   store_dev -- device scope (sc1), written through L2 (combine 191 us
-//                against 198, combine_bwd 389 against 432).
 __device__ __forceinline__ void store_nt(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
-__device__ __forceinline__ void store_wb(u32x4 *p, u32x4 v) { *p = v; }
-
-// store_dev writes lane data at byte `off` of the row starting at `row`, which
-// must be the same for the whole wave, and `row_bytes` long (stores past it
-// are dropped).  It goes through a buffer resource because the buffer-store
-// builtin is the one that takes the scope bits (cache policy 16 = sc1) for 16
-// bytes and lets the compiler insert the wait states a wide store needs
-// before its data registers are reused.  0x00020000 is the gfx9 descriptor
-// word for 32-bit untyped access.
-__device__ __forceinline__ void store_dev(u32x4 *row, uint32_t row_bytes, uint32_t off, u32x4 v)
-{
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(row, 0, (int)row_bytes, 0x00020000);
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 16);
-}
 
 // Exclusive scan over a block of kBlock threads of one int per thread.
 // `tmp` must hold kWaves ints of LDS.  Returns the exclusive prefix; *total

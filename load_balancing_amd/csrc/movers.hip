@@ -17,10 +17,12 @@
 // any use (out-of-range slots read row 0 and are masked afterwards, so no
 // branch splits the loads).  Dispatch paces its stores instead (see there).
 // Loads are non-temporal, which measured faster on gfx950 than cached ones
-// for every mover.  Stores take the policy that measured fastest per kernel
-// from an evicted cache (see store_nt / store_wb / store_dev): write-back for
-// dispatch, device scope for combine and combine_bwd, non-temporal for
-// dispatch_bwd.
+// for every mover.  Stores are non-temporal too: write-back or device-scope
+// stores made a call itself up to 12% shorter, but they left dirty lines in
+// the MALL that the next HBM traffic had to write back.  A call plus the
+// 512 MiB read after it took as long as with non-temporal stores (dispatch
+// 384 us either way, combine 349), so each call's time here includes its own
+// writes to HBM.
 #include "moonep_internal.hpp"
 
 namespace moonep {
@@ -41,18 +43,17 @@ inline int block_for(int32_t V)
 
 // Resident waves per CU that measured best on gfx950 for each mover in the
 // full step on the expert-grouped access pattern, each call starting with
-// the MALL and L2 evicted and with the store policies below (HBM efficiency
-// falls when more scattered row requests are in flight; too few leave it
-// idle): dispatch 16, combine 12, combine_bwd 16, dispatch_bwd 12 -- 4, 3, 4
-// and 3 workgroups of 256 threads.  On the 1.2 GB sweep step: dispatch 199 us
-// at 16 against 207 at 12, 202 at 20 and 230 at 8; combine 190 us at 12
-// against 195 at 16 and 205 at 8; combine_bwd 387 us at 16, the same at 20
-// and 24, 430 at 12; dispatch_bwd, whose fp64 sums need 154 VGPRs, 228 us at
-// 8 and 203 at 12-20.  Rows longer than one workgroup (workgroups of one
-// column block, H = 4096 and 7168) dispatch best at 16 as well: 1608 us
-// against 1719 at 12 on the adversarial shape, 3183 against 3357 on the
-// DeepSeek-V3-like one.
-constexpr int kDispatchWaves = 16, kDispatchBlocksWaves = 16, kCombineWaves = 12,
+// the MALL and L2 evicted (HBM efficiency falls when more scattered row
+// requests are in flight; too few leave it idle): dispatch 12, combine 12,
+// combine_bwd 16, dispatch_bwd 12 -- 3, 3, 4 and 3 workgroups of 256 threads.
+// On the 1.2 GB sweep step: dispatch 225 us at 12 against 231-235 at 8, 16
+// and 20; combine 198 us at 12 against 210 at 8 and 209 at 16; combine_bwd
+// 431 us at 16 against 445 at 12; dispatch_bwd, whose fp64 sums need 154
+// VGPRs, 228 us at 8 and 203 at 12-20.  Dispatch of rows longer than one
+// workgroup (workgroups of one column block, H = 4096 and 7168) does best at
+// 16: 1608 us against 1719 at 12 on the adversarial shape, 3183 against 3357
+// on the DeepSeek-V3-like one (8 waves: 2121 and 3900; 20-24: in between).
+constexpr int kDispatchWaves = 12, kDispatchBlocksWaves = 16, kCombineWaves = 12,
               kCombineBwdWaves = 16, kDispatchBwdWaves = 12;
 
 // Dynamic LDS a workgroup of `threads` requests so that only
@@ -134,7 +135,7 @@ __device__ __forceinline__ void dispatch_column(const u32x4 *__restrict__ x,
     for (int32_t k = 0; k < K; ++k) {
         const uint32_t sk = (uint32_t)so[k];
         if (sk < nrows)
-            store_wb(buf + (int64_t)sk * V + v, val);
+            store_nt(buf + (int64_t)sk * V + v, val);
     }
 }
 
@@ -241,7 +242,7 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const u32x4 *__restrict
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 r[j] = pack_bf16(acc[2 * j], acc[2 * j + 1]);
-            store_dev(y + (int64_t)tok * V, (uint32_t)V * 16u, (uint32_t)v * 16u, r);
+            store_nt(y + (int64_t)tok * V + v, r);
         }
     }
 }
@@ -365,12 +366,12 @@ __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(
             if (all) {
 #pragma unroll
                 for (int c = 0; c < kN; ++c)
-                    store_dev(d_out + (int64_t)sl.s[c] * V, (uint32_t)V * 16u, (uint32_t)v * 16u, r[c]);
+                    store_nt(d_out + (int64_t)sl.s[c] * V + v, r[c]);
             } else {
 #pragma unroll
                 for (int c = 0; c < kN; ++c)
                     if (sl.s[c] != 0xFFFFFFFFu)
-                        store_dev(d_out + (int64_t)sl.s[c] * V, (uint32_t)V * 16u, (uint32_t)v * 16u, r[c]);
+                        store_nt(d_out + (int64_t)sl.s[c] * V + v, r[c]);
             }
         }
 #pragma unroll
