@@ -36,9 +36,12 @@ S=4096, K=8, H=7168, Zipf 1.2, weight-gradients 7168 x 2048) and --workload
 adversarial (R=16, E=128, S=8192, K=8, H=4096, every token to experts 0..7).
 Their multi-GB gradient arrays repeat eight seeded synthetic rows (the
 reduction's time does not depend on the values); their CPU baseline runs the
-oracle's dispatch and combine on a sample of tokens.
+oracle's dispatch and combine on a sample of tokens.  --workload tiny (R=4,
+E=16, S=128, K=2, H=64, Zipf 1.0) times the latency of every call on a shape
+of a few hundred KB; its 64-wide rows are below the grouped GEMM's 128-column
+granularity, so it has no GEMM leg.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload sweep]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload sweep|dsv3|adversarial|tiny]
                     [--no-cpu-baseline]
 """
 import argparse
@@ -69,7 +72,23 @@ WORKLOAD_NAME = {
     "adversarial": "adversarial R16 E128 S8192 K8 H4096, every token to experts 0..7, gates 1/8; "
                    "expert weights 3x4096x2048 bf16 with E/R prefetch slots per rank; backward "
                    "weight-grads 4096x2048 fp32",
+    "tiny": "tiny R4 E16 S128 K2 H64, Zipf 1.0; expert weights 3x64x32 bf16 with E/R prefetch "
+            "slots per rank; backward weight-grads 64x32 fp32",
 }
+
+
+def host_cpu():
+    """(model name, usable cores) of the host the CPU baseline runs on."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
 
 
 def algorithmic_bytes(R, S, K, H, G=0, reps=None):
@@ -127,8 +146,9 @@ def cpu_baseline(levels, seed):
         t_plan += t1 - t0
         t_disp += t2 - t1
         t_comb += t3 - t2
+    model, nproc = host_cpu()
     return {"value": round(dc / (t_disp + t_comb) / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": model, "host_nproc": nproc,
             "sample": f"one forward step at each maxvio level {list(levels)} (seed {seed}), "
                       f"single thread: route_stats+plan+slots {1e3 * t_plan:.1f} ms, dispatch "
                       f"{1e3 * t_disp:.1f} ms, combine {1e3 * t_comb:.1f} ms in total; value = "
@@ -157,8 +177,9 @@ def cpu_baseline_sampled(w, seed, ntok=2048):
     t2 = time.perf_counter()
     b = algorithmic_bytes(w.R, w.S, w.K, w.H)
     per_tok = (b["dispatch"] + b["combine"]) / w.N
+    model, nproc = host_cpu()
     return {"value": round(per_tok * toks.size / (t2 - t0) / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle",
+            "kind": "oracle", "host_cpu": model, "host_nproc": nproc,
             "sample": f"dispatch and combine of {toks.size} random tokens of the workload "
                       f"(seed {seed}), single thread: {1e3 * (t1 - t0):.1f} ms + "
                       f"{1e3 * (t2 - t1):.1f} ms; value = their share of the algorithmic "
@@ -265,7 +286,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", default="sweep", choices=("sweep", "dsv3", "adversarial"))
+    ap.add_argument("--workload", default="sweep", choices=("sweep", "dsv3", "adversarial", "tiny"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-expert-gemm", action="store_true",
                     help="skip the timed grouped-GEMM leg after the steps")
@@ -415,6 +436,7 @@ def main():
             per_level[lv][name].append(ms)
     mean = lambda v: sum(v) / len(v)
     us = {c: round(1e3 * mean(v), 2) for c, v in per_call.items()}
+    med = {c: round(1e3 * sorted(v)[len(v) // 2], 2) for c, v in per_call.items()}
 
     byt = algorithmic_bytes(R, S, K, H)
     dc_bytes = byt["dispatch"] + byt["combine"]
@@ -486,6 +508,7 @@ def main():
                     "queued behind a 40 us copy so no launch gap is timed",
         "plan_us_in_step": plan_us_in_step,
         "breakdown_us": us,
+        "breakdown_median_us": med,
         "kernels": kern,
         "replicas_per_level": {lv: int(sum(r)) for lv, r in zip(levels, reps_per_level)},
         "prefetch": {"B": B_slots, "weight_bytes_per_expert": wbytes,
@@ -494,7 +517,10 @@ def main():
                                             zip(levels, reps_per_level, pref_per_level)}},
         "roofline": roof,
     }
-    if not args.no_expert_gemm:
+    if args.workload == "tiny":
+        result["expert_gemm"] = {"skipped": "H = 64 is below the grouped GEMM's 128-column "
+                                            "granularity"}
+    elif not args.no_expert_gemm:
         result["expert_gemm"] = expert_gemm_leg(mx, s, b, wslot, B_slots, w_home, pool, wbytes,
                                                 d_out, max(1, min(args.steps, 20)), stream,
                                                 gemm_traffic(args.workload))

@@ -17,9 +17,16 @@
 //
 // Kernel: a persistent grid, one workgroup per CU.  Every workgroup first
 // scans the per-segment tile counts into LDS (n_rep is known only on the
-// device), then walks (tile, column-block) items.  The items of each XCD are
-// one contiguous range, so the workgroups running together on one XCD share
-// their row tile and the segment's weights in that XCD's L2.  Per item: BM x BN
+// device), then walks (tile, column-block) items.  Items are numbered in
+// groups of kGroupM row tiles, the row tile running fastest inside a group,
+// so any run of 32 consecutive items covers 8 row tiles and 4 column blocks
+// (12 distinct operand slices per k-step instead of up to 29 when the column
+// block runs fastest on a wide output).  The grid walks them in rounds of
+// gridDim items, each XCD taking one run of consecutive items per round:
+// the workgroups running together on one XCD share their A and B slices in
+// that XCD's L2, and all XCDs stay within one window of the item space, so
+// the weights they read at the same time are those of one or two segments
+// and stay in the MALL.  Per item: BM x BN
 // outputs; K advances BK at a time through a ring of S LDS stages filled by
 // LDS-DMA (global_load_lds_dwordx4: no staging registers), with the 16-byte
 // chunks of each row XOR-swizzled so that fragment reads are free of bank
@@ -39,6 +46,11 @@ namespace moonep {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Row tiles per item group (the item order of the grouped GEMM).  Measured
+// against 4 and against no grouping: best on the wide DeepSeek-V3-like
+// projections, no change on the 2048-wide ones.
+constexpr int kGroupM = 8;
 
 template <int BM, int BN, int WM, int WN, int BK, int S>
 struct GemmCfg {
@@ -159,20 +171,28 @@ __global__ __launch_bounds__((GemmCfg<BM, BN, WM, WN, BK, S>::kThreads)) void ex
     // ---- items of this workgroup's XCD -------------------------------------
     const int32_t nbn = (a.out_dim + BN - 1) / BN;  // the last block may be part-empty
     const int64_t items = (int64_t)total_tiles * nbn;
+    // workgroup b runs on XCD b % 8; the XCD-x workgroups take the slots
+    // after those of XCDs 0..x-1 in each round (XCD x holds ceil((P - x)/8))
     const int xcd = (int)(blockIdx.x % 8), q = (int)(blockIdx.x / 8);
-    const int gx = ((int)gridDim.x - xcd + 7) / 8;
-    const int64_t span = (items + 7) / 8;
-    const int64_t lo = (int64_t)xcd * span;
-    const int64_t hi = lo + span < items ? lo + span : items;
+    const int P = (int)gridDim.x;
+    int slot = q;
+    for (int x = 0; x < xcd; ++x)
+        slot += (P - x + 7) / 8;
     const int32_t nk = a.in_dim / G::kBK;
     const int wm = wave / G::kWN, wn = wave % G::kWN;
     int log_nseg = 0;
     while ((1 << log_nseg) < nseg + 1)
         ++log_nseg;
 
-    for (int64_t it = lo + q; it < hi; it += gx) {
-        const int32_t t = (int32_t)(it / nbn);
-        const int32_t nb = (int32_t)(it - (int64_t)t * nbn);
+    for (int64_t it = slot; it < items; it += P) {
+        // item -> (row tile t, column block nb): group gi holds row tiles
+        // [gi*kGroupM, gi*kGroupM + gm), gm < kGroupM only for the last group
+        const int64_t gi = it / ((int64_t)kGroupM * nbn);
+        const int32_t within = (int32_t)(it - gi * ((int64_t)kGroupM * nbn));
+        const int32_t gleft = total_tiles - (int32_t)gi * kGroupM;
+        const int32_t gm = gleft < kGroupM ? gleft : kGroupM;
+        const int32_t t = (int32_t)gi * kGroupM + within % gm;
+        const int32_t nb = within / gm;
         // segment holding tile t: last s with seg_start[s] <= t (fixed-depth search)
         int32_t s = 0;
         for (int b = log_nseg - 1; b >= 0; --b) {
