@@ -31,6 +31,12 @@ namespace {
 
 constexpr int KC = 8;  // experts per token handled per pass (registers)
 
+// Largest grid a mover launches, in workgroups; larger problems loop over the
+// grid (or, for combine_bwd, take several launches).  A dispatch carries its
+// size in work-items as a 32-bit number, and 2^22 workgroups of up to 256
+// threads stay well inside it.
+constexpr int64_t kMaxGrid = (int64_t)1 << 22;
+
 // Largest workgroup size in {256, 128, 64} that divides V (64 if none).
 inline int block_for(int32_t V)
 {
@@ -312,15 +318,19 @@ __global__ __launch_bounds__(kBlock) void dispatch_bwd_kernel(const u32x4 *__res
 // d_out[slot_of[n]] = bf16(g_n * dy[tok]) (exact product, one rounding);
 // d_gates[n] = <dy[tok], out[slot_of[n]]> in fp32: per-thread partial dots
 // over its columns, then a wave butterfly and a cross-wave sum in LDS.
-template <int KT>
+// Workgroup b handles token b, or tok0 + b in the launches of a problem
+// larger than one grid (kChunked: the token offset costs each workgroup's
+// prologue a dependent load, measured 2-7% on the sweep, so only those
+// launches pay it).
+template <int KT, bool kChunked>
 __global__ __launch_bounds__(kBlock) void combine_bwd_kernel(
     const u32x4 *__restrict__ dy, const u32x4 *__restrict__ out, const float *__restrict__ gates,
     const int32_t *__restrict__ slot_of, u32x4 *__restrict__ d_out, float *__restrict__ d_gates,
-    int32_t V, int32_t K, uint32_t nrows)
+    int64_t tok0, int32_t V, int32_t K, uint32_t nrows)
 {
     constexpr int kN = Slots<KT>::kN;
     __shared__ float red[kN][kWaves];
-    const int64_t tok = blockIdx.x;
+    const int64_t tok = kChunked ? tok0 + (int64_t)blockIdx.x : (int64_t)blockIdx.x;
     const int32_t *so = slot_of + tok * K;
     const float *gt = gates + tok * K;
     const int lane = lane_id();
@@ -426,11 +436,16 @@ void run_dispatch_bwd(dim3 g, dim3 b, hipStream_t st, const u32x4 *d_buf, const 
 
 template <int KT>
 void run_combine_bwd(dim3 g, dim3 b, hipStream_t st, const u32x4 *dy, const u32x4 *out,
-                     const float *gates, const int32_t *so, u32x4 *d_out, float *d_gates, int32_t V,
-                     int32_t K, uint32_t nrows)
+                     const float *gates, const int32_t *so, u32x4 *d_out, float *d_gates,
+                     int64_t total, int64_t tok0, int32_t V, int32_t K, uint32_t nrows)
 {
-    hipLaunchKernelGGL(combine_bwd_kernel<KT>, g, b, residency_lds(kCombineBwdWaves, (int)b.x), st, dy,
-                       out, gates, so, d_out, d_gates, V, K, nrows);
+    const size_t lds = residency_lds(kCombineBwdWaves, (int)b.x);
+    if (tok0 == 0 && g.x == total)
+        hipLaunchKernelGGL((combine_bwd_kernel<KT, false>), g, b, lds, st, dy, out, gates, so, d_out,
+                           d_gates, tok0, V, K, nrows);
+    else
+        hipLaunchKernelGGL((combine_bwd_kernel<KT, true>), g, b, lds, st, dy, out, gates, so, d_out,
+                           d_gates, tok0, V, K, nrows);
 }
 
 int launch_dispatch(const moonep_shape &s, const uint16_t *x, const int32_t *slot_of, uint16_t *buf,
@@ -444,7 +459,7 @@ int launch_dispatch(const moonep_shape &s, const uint16_t *x, const int32_t *slo
     const int bs = block_for(V);
     const int32_t ncb = (V + bs - 1) / bs;
     const int64_t total = N * ncb;
-    const uint32_t grid = (uint32_t)(total < (1 << 24) ? total : (1 << 24));
+    const uint32_t grid = (uint32_t)(total < kMaxGrid ? total : kMaxGrid);
     const size_t lds = residency_lds(ncb == 1 ? kDispatchWaves : kDispatchBlocksWaves, bs);
     if (ncb == 1)
         hipLaunchKernelGGL(dispatch_kernel, dim3(grid, 1), dim3(bs), lds, st, (const u32x4 *)x,
@@ -468,7 +483,7 @@ int launch_combine(const moonep_shape &s, const uint16_t *out, const float *gate
     const int32_t cpb = ncb < 4 ? ncb : 1;  // column blocks per workgroup
     const int32_t nwb = (ncb + cpb - 1) / cpb;
     const int64_t total = N * nwb;
-    const uint32_t grid = (uint32_t)(total < (1 << 24) ? total : (1 << 24));
+    const uint32_t grid = (uint32_t)(total < kMaxGrid ? total : kMaxGrid);
     MOONEP_BY_K(s.K, run_combine, dim3(grid), dim3(bs), st, (const u32x4 *)out, gates, slot_of,
                 (u32x4 *)y, N, V, nwb, cpb, s.K, nrows);
     return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
@@ -487,7 +502,7 @@ int launch_dispatch_bwd(const moonep_shape &s, const uint16_t *d_buf, const int3
     const int32_t cpb = ncb < 4 ? ncb : 1;  // column blocks per workgroup, as combine
     const int32_t nwb = (ncb + cpb - 1) / cpb;
     const int64_t total = N * nwb;
-    const uint32_t grid = (uint32_t)(total < (1 << 24) ? total : (1 << 24));
+    const uint32_t grid = (uint32_t)(total < kMaxGrid ? total : kMaxGrid);
     MOONEP_BY_K(s.K, run_dispatch_bwd, dim3(grid), dim3(bs), st, (const u32x4 *)d_buf, slot_of,
                 (u32x4 *)dx, N, V, nwb, cpb, s.K, nrows);
     return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
@@ -502,10 +517,18 @@ int launch_combine_bwd(const moonep_shape &s, const uint16_t *dy, const uint16_t
         return MOONEP_OK;
     const int32_t V = s.H / 8;
     const uint32_t nrows = (uint32_t)(N * s.K);
-    MOONEP_BY_K(s.K, run_combine_bwd, dim3((uint32_t)N), dim3(block_for(V)), st,
-                (const u32x4 *)dy, (const u32x4 *)out, gates, slot_of, (u32x4 *)d_out, d_gates, V,
-                s.K, nrows);
-    return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
+    // one token per workgroup, in launches of at most kMaxGrid tokens (a
+    // grid-stride loop here would cost the kernel registers it cannot spare
+    // at its residency)
+    for (int64_t t0 = 0; t0 < N; t0 += kMaxGrid) {
+        const uint32_t grid = (uint32_t)(N - t0 < kMaxGrid ? N - t0 : kMaxGrid);
+        MOONEP_BY_K(s.K, run_combine_bwd, dim3(grid), dim3(block_for(V)), st, (const u32x4 *)dy,
+                    (const u32x4 *)out, gates, slot_of, (u32x4 *)d_out, d_gates, N, t0, V, s.K,
+                    nrows);
+        if (hipGetLastError() != hipSuccess)
+            return MOONEP_ERR_HIP;
+    }
+    return MOONEP_OK;
 }
 
 }  // namespace moonep

@@ -192,6 +192,22 @@ def test_shape_limits(w):
     assert r["n_rep"] > 0
 
 
+# More than 2^22 tokens: the movers' grids are capped at 2^22 workgroups, so
+# dispatch, combine and dispatch_bwd loop over their grid and combine_bwd runs
+# in two launches.  Rows of 8 elements keep every array small.
+MANY_TOKENS = [
+    synth.Workload("many_tokens_k1", 8, 16, 540000, 1, 8, "zipf", alpha=1.0, G=8),
+    synth.Workload("many_tokens_k2", 4, 16, 1050000, 2, 8, "zipf", alpha=1.0, G=8),
+]
+
+
+@pytest.mark.parametrize("w", MANY_TOKENS, ids=lambda w: w.name)
+def test_more_tokens_than_one_grid(w):
+    assert w.N > 1 << 22
+    r = run_and_compare(w, 0)
+    assert r["n_rep"] > 0
+
+
 def test_bad_expert_id_sets_error_word_and_stays_in_bounds():
     w = synth.WORKLOADS["tiny"]
     topk, gates = synth.routing(w, 0)
