@@ -256,7 +256,7 @@ int moonep_prefetch_weights(const moonep_shape *shape, const int32_t *plan, cons
  * expert e; for replica j, pool + wslot[j]*w_stride when 0 <= wslot[j] < R*B,
  * else w_home + rep_expert[j]*w_stride.  w_home holds E weight rows, pool R*B
  * (the layouts of moonep_prefetch_weights, counted in bf16 elements here).
- * Limits (else MOONEP_ERR_ARG): in_dim % 64 == 0, out_dim % 128 == 0,
+ * Limits (else MOONEP_ERR_ARG): in_dim % 64 == 0, in_dim <= 2^22, out_dim % 128 == 0,
  * w_stride and w_offset multiples of 8, w_offset + out_dim*in_dim <= w_stride.
  * x, y, w_home, pool 16-byte aligned; y must not overlap x, w_home or pool.
  */

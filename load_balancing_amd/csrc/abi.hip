@@ -300,9 +300,12 @@ int moonep_expert_gemm(const moonep_shape *shape, const int32_t *plan, const int
     int rc = shape_status(shape);
     if (rc != MOONEP_OK)
         return rc;
+    // the kernel addresses a row of a tile by a 32-bit byte offset: 256 rows of in_dim bf16
+    constexpr int32_t kMaxInDim = 1 << 22;
     if (B < 0 || (int64_t)shape->R * B >= ((int64_t)1 << 31) || in_dim <= 0 || in_dim % 64 != 0 ||
-        out_dim <= 0 || out_dim % gemm_out_align() != 0 || w_stride % 8 != 0 || w_offset < 0 ||
-        w_offset % 8 != 0 || w_offset + (int64_t)out_dim * in_dim > w_stride)
+        in_dim > kMaxInDim || out_dim <= 0 || out_dim % gemm_out_align() != 0 ||
+        w_stride % 8 != 0 || w_offset < 0 || w_offset % 8 != 0 ||
+        w_offset + (int64_t)out_dim * in_dim > w_stride)
         return MOONEP_ERR_ARG;
     const int64_t rows = n_entries(shape);
     const int64_t pool_rows = (int64_t)shape->R * B;

@@ -104,6 +104,18 @@ def test_host_errors_before_any_launch(L):
                                      vp(fake * 4 + 256), None) == -6
     assert L.moonep_prefetch_weights(B(s), vp(fake), vp(fake * 2), 2, i64(32), None,
                                      vp(fake * 8), None) == -2
+    # expert GEMM: dimension rules, weight window past the row, null, misaligned, overlap
+    g = lambda kin, kout, x, y, w_stride=i64(128 * 64), w_off=i64(0), wh=vp(fake * 4): \
+        L.moonep_expert_gemm(B(s), vp(fake), vp(fake * 2), 2, kin, kout, x, wh, vp(fake * 8),
+                             w_stride, w_off, y, None)
+    assert g(96, 128, vp(fake * 16), vp(fake * 32)) == -7          # in_dim % 64
+    assert g(64, 192, vp(fake * 16), vp(fake * 32)) == -7          # out_dim % 128
+    assert g((1 << 22) + 64, 128, vp(fake * 16), vp(fake * 32),
+             w_stride=i64(((1 << 22) + 64) * 128)) == -7           # in_dim above 2^22
+    assert g(64, 128, vp(fake * 16), vp(fake * 32), w_off=i64(8)) == -7  # window past the row
+    assert g(64, 128, None, vp(fake * 32)) == -2
+    assert g(64, 128, vp(fake * 16 + 8), vp(fake * 32)) == -3
+    assert g(64, 128, vp(fake * 16), vp(fake * 16 + 64)) == -6     # y overlaps x
     # invalid shape is reported first
     bad = mx.Shape(3, 16, 128, 2, 64)
     assert L.moonep_dispatch(B(bad), vp(fake), vp(fake), vp(fake * 4), None) == -1
