@@ -179,10 +179,15 @@ def test_gemm_sweep_full_size(proj):
         full_size(w, F, w.H, 2 * w.H * F, 0, 256)
 
 
-def test_gemm_dsv3_full_size():
-    """DeepSeek-V3-like shape, gate projection 7168 -> 2048 over the 1M-row
-    dispatch buffer (training B = E/R slots, one overflow replica); sampled
-    rows against the oracle."""
+@pytest.mark.parametrize("proj", ["gate", "down"])
+def test_gemm_dsv3_full_size(proj):
+    """DeepSeek-V3-like shape over 1M rows (training B = E/R slots, one
+    overflow replica): the gate projection 7168 -> 2048 of the dispatch
+    buffer, and the down projection 2048 -> 7168, whose 28 column blocks
+    make the widest item groups; sampled rows against the oracle."""
     w = synth.WORKLOADS["dsv3"]
-    print(f"[case] {w.name} gate", flush=True)
-    full_size(w, w.H, 2048, 0, 0, 96, single=True)
+    print(f"[case] {w.name} {proj}", flush=True)
+    if proj == "gate":
+        full_size(w, w.H, 2048, 0, 0, 96, single=True)
+    else:
+        full_size(w, 2048, w.H, 0, 0, 96, single=True)
