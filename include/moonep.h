@@ -29,7 +29,9 @@
  *
  * Conventions shared by every call:
  *  - All array arguments are DEVICE pointers owned by the caller; the library
- *    allocates nothing and keeps no state between calls.
+ *    allocates nothing.  Between calls it keeps only the CU's LDS size (read
+ *    once per process) and, per device, whether one kernel's dynamic-LDS limit
+ *    has been raised for large E and R.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Every
  *    call only enqueues work; none waits for the device, except
  *    moonep_read_error.  Output sizes depend on the shape alone, so no call
