@@ -18,7 +18,13 @@ constexpr int kMaxExperts = 1024;  // on-chip plan tables
 constexpr int kMaxRanks = 512;
 constexpr int kBlock = 256;        // threads per workgroup (4 waves of 64)
 constexpr int kWaves = kBlock / 64;
-constexpr int kTargetSegments = 1024;  // one wave per segment; ~1 wave per SIMD
+// Wave segments (one wave each) for route_stats and the plan: NK / 512 of
+// them, kept between 1024 and 2048.  route_stats + plan measured best so on
+// gfx950: 1024 segments of 256 entries on a 262K-entry routing (27.4 us,
+// against 28.2 at 2048 and 30-31 at 512), 2048 of 512 entries on 1M-entry
+// ones (57.5 us against 60.7 at 1024 and 65.6 at 4096 on the 256-expert
+// shape; 42.0 against 46.4 and 45.9 on the 128-expert one).
+constexpr int kMinSegments = 1024, kMaxSegments = 2048, kSegmentEntries = 512;
 constexpr int kChunkBatch = 16;        // 64-entry chunks loaded ahead per wave
 constexpr size_t kCtlBytes = 256;      // workspace control block
 
@@ -37,7 +43,9 @@ inline WsLayout ws_layout(const moonep_shape &s)
 {
     WsLayout w{};
     w.nk = (int64_t)s.R * s.S * s.K;
-    int64_t per = (w.nk + kTargetSegments - 1) / kTargetSegments;
+    int64_t target = w.nk / kSegmentEntries;
+    target = target < kMinSegments ? kMinSegments : (target > kMaxSegments ? kMaxSegments : target);
+    int64_t per = (w.nk + target - 1) / target;
     per = ((per + 63) / 64) * 64;
     if (per < 64)
         per = 64;

@@ -80,18 +80,19 @@ __global__ __launch_bounds__(kBlock) void rs_scan_kernel(int32_t *__restrict__ h
     __shared__ int red[kWaves];
     const int e = (int)blockIdx.x;
     int32_t *col = hist + (int64_t)e * nseg;
-    const int per = (nseg + kBlock - 1) / kBlock;  // <= 4 with kTargetSegments = 1024
+    constexpr int kPer = kMaxSegments / kBlock;    // entries per thread, at most
+    const int per = (nseg + kBlock - 1) / kBlock;  // <= kPer
     const int first = (int)threadIdx.x * per;
-    int local[4] = {0, 0, 0, 0};
+    int local[kPer] = {};
     int sum = 0;
-    for (int i = 0; i < per && i < 4; ++i) {
+    for (int i = 0; i < per && i < kPer; ++i) {
         const int s = first + i;
         local[i] = s < nseg ? col[s] : 0;
         sum += local[i];
     }
     int total = 0;
     int run = block_exclusive_scan(sum, tmp, &total);
-    for (int i = 0; i < per && i < 4; ++i) {
+    for (int i = 0; i < per && i < kPer; ++i) {
         const int s = first + i;
         if (s < nseg)
             col[s] = run;

@@ -257,8 +257,9 @@ def test_repeat_is_bitwise_deterministic():
 
 
 def test_plan_with_several_chunk_batches_per_wave():
-    # 2M entries: each wave walks two batches of 16 chunks
-    w = synth.Workload("long_segments", 16, 64, 16384, 8, 8, "zipf", alpha=1.1)
+    # 4.2M entries: 2048 segments of 2048 entries, so each wave walks two
+    # batches of 16 chunks
+    w = synth.Workload("long_segments", 16, 64, 32768, 8, 8, "zipf", alpha=1.1)
     topk, _ = synth.routing(w, 0)
     T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk)
     s = shape_of(w)
