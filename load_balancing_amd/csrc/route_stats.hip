@@ -84,19 +84,53 @@ __global__ __launch_bounds__(kBlock) void rs_scan_kernel(int32_t *__restrict__ h
     const int per = (nseg + kBlock - 1) / kBlock;  // <= kPer
     const int first = (int)threadIdx.x * per;
     int local[kPer] = {};
-    int sum = 0;
-    for (int i = 0; i < per && i < kPer; ++i) {
-        const int s = first + i;
-        local[i] = s < nseg ? col[s] : 0;
-        sum += local[i];
+    // 16-byte groups when each thread's run is whole groups (per and nseg
+    // multiples of 4: a group then lies wholly inside or outside the column,
+    // and col is 16-byte aligned); single counts otherwise
+    const bool vec = (per & 3) == 0 && (nseg & 3) == 0;
+    if (vec) {
+#pragma unroll
+        for (int c = 0; c < kPer / 4; ++c) {
+            const int s = first + 4 * c;
+            if (4 * c < per && s < nseg) {
+                const int4 v = *(const int4 *)(col + s);
+                local[4 * c] = v.x;
+                local[4 * c + 1] = v.y;
+                local[4 * c + 2] = v.z;
+                local[4 * c + 3] = v.w;
+            }
+        }
+    } else {
+        for (int i = 0; i < per && i < kPer; ++i) {
+            const int s = first + i;
+            local[i] = s < nseg ? col[s] : 0;
+        }
     }
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i)
+        sum += local[i];
     int total = 0;
     int run = block_exclusive_scan(sum, tmp, &total);
-    for (int i = 0; i < per && i < kPer; ++i) {
-        const int s = first + i;
-        if (s < nseg)
-            col[s] = run;
+    int ex[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        ex[i] = run;
         run += local[i];
+    }
+    if (vec) {
+#pragma unroll
+        for (int c = 0; c < kPer / 4; ++c) {
+            const int s = first + 4 * c;
+            if (4 * c < per && s < nseg)
+                *(int4 *)(col + s) = make_int4(ex[4 * c], ex[4 * c + 1], ex[4 * c + 2], ex[4 * c + 3]);
+        }
+    } else {
+        for (int i = 0; i < per && i < kPer; ++i) {
+            const int s = first + i;
+            if (s < nseg)
+                col[s] = ex[i];
+        }
     }
     if (threadIdx.x == 0) {
         counts[e] = total;
