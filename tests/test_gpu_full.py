@@ -137,10 +137,13 @@ def test_adversarial_forward_sampled():
     assert r["exact"] > 0.99
 
 
-def test_dsv3_backward_sampled():
-    """Combine backward and the replica-gradient reduction at the
-    DeepSeek-V3-like shape with 7168 x 2048 expert weight-gradients."""
-    w = synth.WORKLOADS["dsv3_bwd"]
+@pytest.mark.parametrize("name", ["dsv3_bwd", "adversarial"])
+def test_backward_sampled(name):
+    """Combine backward, dispatch backward and the replica-gradient reduction
+    at full size: the DeepSeek-V3-like shape with 7168 x 2048 expert
+    weight-gradients, and the adversarial shape (every token to experts 0..7,
+    15 replicas) with 4096 x 2048 ones."""
+    w = synth.WORKLOADS[name]
     print(f"[case] {w.name}", flush=True)
     seed = 0
     topk, gates = synth.routing(w, seed)
