@@ -191,3 +191,12 @@ def test_gemm_dsv3_full_size(proj):
         full_size(w, w.H, 2048, 0, 0, 96, single=True)
     else:
         full_size(w, 2048, w.H, 0, 0, 96, single=True)
+
+
+def test_gemm_adversarial_full_size():
+    """Adversarial shape: every row belongs to experts 0..7 or their 15
+    replicas (all in prefetch slots at B = E/R); the 4096 -> 2048 projection
+    of the dispatch buffer on sampled rows."""
+    w = synth.WORKLOADS["adversarial"]
+    print(f"[case] {w.name}", flush=True)
+    full_size(w, w.H, 2048, 0, 0, 96, single=True)
