@@ -133,11 +133,11 @@ def test_gemm_real_inputs_within_bound(case):
     print(f"[{w.name}] equal to the oracle: {exact:.4f}")
 
 
-def full_size(w, kin, kout, off, seed, nsample, single=False):
+def full_size(w, kin, kout, off, seed, nsample, single=False, B=None):
     """The dispatch buffer of the workload times its experts' weights (rows of
     gate, up, down: 3 * H * F bf16, or one projection if single), checked on
-    sampled rows."""
-    B = w.E // w.R
+    sampled rows; B prefetch slots per rank (training E/R by default)."""
+    B = w.E // w.R if B is None else B
     s, b, pl, ws, o_ws = setup(w, seed, B)
     H, F = w.H, kout if off == 0 else kin
     stride = kin * kout if single else 3 * H * F
@@ -191,6 +191,15 @@ def test_gemm_dsv3_full_size(proj):
         full_size(w, w.H, 2048, 0, 0, 96, single=True)
     else:
         full_size(w, 2048, w.H, 0, 0, 96, single=True)
+
+
+def test_gemm_dsv3_inference_slots():
+    """DeepSeek-V3-like gate projection with B = 3 prefetch slots per rank (an
+    inference setting): 21 of the 61 replicas overflow and read their weights
+    at the home expert."""
+    w = synth.WORKLOADS["dsv3"]
+    print(f"[case] {w.name} gate B=3", flush=True)
+    full_size(w, w.H, 2048, 0, 0, 96, single=True, B=3)
 
 
 def test_gemm_adversarial_full_size():
