@@ -137,6 +137,70 @@ __device__ int wave_scan_array(const int32_t *in, int32_t *out, int n)
     return total;
 }
 
+// Four independent exclusive scans in one pass, so that their shuffle chains
+// interleave: in0/in1 over n01 entries, in2/in3 over n23 entries, each laid
+// out as in wave_scan_array (out[n] = total).  Returns the totals of in1 and
+// in3 (the list lengths when those are 0/1 flags).
+__device__ void wave_scan_arrays4(const int32_t *in0, int32_t *out0, const int32_t *in1,
+                                  int32_t *out1, int n01, const int32_t *in2, int32_t *out2,
+                                  const int32_t *in3, int32_t *out3, int n23, int *tot1, int *tot3)
+{
+    const int lane = lane_id();
+    const int pa = (n01 + 63) / 64, pb = (n23 + 63) / 64;
+    const int fa = lane * pa, fb = lane * pb;
+    int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
+    for (int i = 0; i < pa; ++i)
+        if (fa + i < n01) {
+            s0 += in0[fa + i];
+            s1 += in1[fa + i];
+        }
+    for (int i = 0; i < pb; ++i)
+        if (fb + i < n23) {
+            s2 += in2[fb + i];
+            s3 += in3[fb + i];
+        }
+    int c0 = s0, c1 = s1, c2 = s2, c3 = s3;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int o0 = __shfl_up(c0, d, 64), o1 = __shfl_up(c1, d, 64);
+        const int o2 = __shfl_up(c2, d, 64), o3 = __shfl_up(c3, d, 64);
+        if (lane >= d) {
+            c0 += o0;
+            c1 += o1;
+            c2 += o2;
+            c3 += o3;
+        }
+    }
+    const int t0 = __shfl(c0, 63, 64), t1 = __shfl(c1, 63, 64);
+    const int t2 = __shfl(c2, 63, 64), t3 = __shfl(c3, 63, 64);
+    int r0 = c0 - s0, r1 = c1 - s1, r2 = c2 - s2, r3 = c3 - s3;
+    for (int i = 0; i < pa; ++i)
+        if (fa + i < n01) {
+            const int v0 = in0[fa + i], v1 = in1[fa + i];
+            out0[fa + i] = r0;
+            out1[fa + i] = r1;
+            r0 += v0;
+            r1 += v1;
+        }
+    for (int i = 0; i < pb; ++i)
+        if (fb + i < n23) {
+            const int v2 = in2[fb + i], v3 = in3[fb + i];
+            out2[fb + i] = r2;
+            out3[fb + i] = r3;
+            r2 += v2;
+            r3 += v3;
+        }
+    if (lane == 0) {
+        out0[n01] = t0;
+        out1[n01] = t1;
+        out2[n23] = t2;
+        out3[n23] = t3;
+    }
+    wave_sync();
+    *tot1 = t1;
+    *tot3 = t3;
+}
+
 // Number of values of the strictly increasing a[0..n) below x, with a fixed
 // number of steps (2^steps > every n this is called with), so that the time
 // does not depend on n.
@@ -201,10 +265,8 @@ __device__ void wave_plan(const PlanLds &S, const int32_t *__restrict__ counts, 
         S.sflag[e] = give > 0 ? 1 : 0;
     }
     wave_sync();
-    wave_scan_array(S.spill, S.Sp, E);
-    const int nA = wave_scan_array(S.sflag, S.sidx, E);
-    wave_scan_array(S.D, S.Dp, R);
-    const int nB = wave_scan_array(S.dflag, S.didx, R);
+    int nA = 0, nB = 0;
+    wave_scan_arrays4(S.spill, S.Sp, S.sflag, S.sidx, E, S.D, S.Dp, S.dflag, S.didx, R, &nA, &nB);
 
     // compact the spill (A) and deficit (B) lists
     for (int e = lane; e < E; e += 64) {
