@@ -273,6 +273,52 @@ def test_plan_with_several_chunk_batches_per_wave():
     np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot)
 
 
+def test_two_streams_with_own_workspaces():
+    """Two layers' route_stats, plan, dispatch and combine on two streams at
+    once, each with its own buffers and workspace, interleaved call by call:
+    each equals the same layer run alone, bit for bit."""
+    w = synth.Workload("streams", 8, 64, 512, 8, 64, "zipf", alpha=1.2)
+    s = shape_of(w)
+    ins = []
+    for seed in (3, 4):
+        topk, gates = synth.routing(w, seed)
+        ins.append((to_dev(topk), to_dev(gates), bf16_dev(synth.activations(w, seed))))
+
+    def layer_calls(b, tk, gt, x, y, st):
+        return [lambda: mx.moonep_route_stats(s, tk, b.expert_counts, b.maxvio, b.workspace, st),
+                lambda: mx.moonep_plan(s, tk, b.expert_counts, b.workspace, b.plan, b.slot_of,
+                                       b.src_of_slot, st),
+                lambda: mx.moonep_dispatch(s, x, b.slot_of, b.buf, st),
+                lambda: mx.moonep_combine(s, b.buf, gt, b.slot_of, y, st)]
+
+    def snap(b, y):
+        return [t.cpu().numpy().copy() for t in (b.plan, b.slot_of, b.src_of_slot,
+                                                 b.buf.view(torch.int16), y.view(torch.int16))]
+
+    alone = []
+    for tk, gt, x in ins:
+        b = mx.allocate(s)
+        y = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
+        for c in layer_calls(b, tk, gt, x, y, None):
+            c()
+        torch.cuda.synchronize()
+        alone.append(snap(b, y))
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]   # default priority
+    bufs = [mx.allocate(s) for _ in ins]
+    ys = [torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda") for _ in ins]
+    torch.cuda.synchronize()
+    for rep in range(3):
+        calls = [layer_calls(bufs[i], *ins[i], ys[i], streams[i]) for i in range(2)]
+        for c0, c1 in zip(*calls):
+            c0()
+            c1()
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert mx.moonep_read_error(bufs[i].workspace) == 0
+            for got, want in zip(snap(bufs[i], ys[i]), alone[i]):
+                np.testing.assert_array_equal(got, want, err_msg=f"rep {rep} layer {i}")
+
+
 def test_plan_random_shapes():
     """Plan, counts, maxvio and slot maps on 300 random small shapes (skews
     from uniform to one hot expert), bit-exact against the oracle."""
