@@ -273,6 +273,26 @@ def test_plan_with_several_chunk_batches_per_wave():
     np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot)
 
 
+@pytest.mark.parametrize("S,nseg", [(1000, 1000), (9500, 1900)])
+def test_plan_partial_scan_groups(S, nseg):
+    """Segment counts that are a multiple of 4 but leave the last threads of
+    the column scan past the end (4 and 8 counts per thread): the 16-byte
+    scan path with a partial last group."""
+    w = synth.Workload(f"scan_groups_{nseg}", 8 if S == 1000 else 16, 64, S, 8, 8, "zipf", alpha=1.1)
+    s = shape_of(w)
+    assert (mx.moonep_workspace_bytes(s) - 256) // (4 * w.E) == nseg
+    topk, _ = synth.routing(w, 0)
+    T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk)
+    b = mx.allocate(s)
+    mx.plan_step(b, to_dev(topk))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(b.expert_counts.cpu().numpy(), T)
+    assert b.maxvio.item() == mv
+    compare_plan(b.plan_fields(), pl, w.E, w.R)
+    np.testing.assert_array_equal(b.slot_of.cpu().numpy(), slot_of)
+    np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot)
+
+
 def test_two_streams_with_own_workspaces():
     """Two layers' route_stats, plan, dispatch and combine on two streams at
     once, each with its own buffers and workspace, interleaved call by call:
