@@ -56,10 +56,13 @@ inline int block_for(int32_t V)
 // and 20; combine 198 us at 12 against 210 at 8 and 209 at 16; combine_bwd
 // 431 us at 16 against 445 at 12; dispatch_bwd, whose fp64 sums need 154
 // VGPRs, 228 us at 8 and 203 at 12-20.  Dispatch of rows longer than one
-// workgroup (workgroups of one column block, H = 4096 and 7168) does best at
-// 16: 1608 us against 1719 at 12 on the adversarial shape, 3183 against 3357
-// on the DeepSeek-V3-like one (8 waves: 2121 and 3900; 20-24: in between).
-constexpr int kDispatchWaves = 12, kDispatchBlocksWaves = 16, kCombineWaves = 12,
+// 256-thread workgroup (H = 4096 and 7168) runs one 64-thread workgroup per
+// 1 KiB column block at 24: 3077 us on the DeepSeek-V3-like shape and 1591
+// on the adversarial one, against 3180 and 1613 with 128- and 256-thread
+// blocks at 16, the best of those (64 threads at 16: 3365 and 1552; at 32:
+// 3600 and 1910).  Rows of one block (H = 2048) stay one 256-thread
+// workgroup: 228-234 us against 239-249 for 64- or 128-thread blocks.
+constexpr int kDispatchWaves = 12, kDispatchBlocksWaves = 24, kCombineWaves = 12,
               kCombineBwdWaves = 16, kDispatchBwdWaves = 12;
 
 // Dynamic LDS a workgroup of `threads` requests so that only
@@ -456,8 +459,13 @@ int launch_dispatch(const moonep_shape &s, const uint16_t *x, const int32_t *slo
         return MOONEP_OK;
     const int32_t V = s.H / 8;
     const uint32_t nrows = (uint32_t)(N * s.K);
-    const int bs = block_for(V);
-    const int32_t ncb = (V + bs - 1) / bs;
+    // one workgroup per row when a row fits one; otherwise 64-thread blocks
+    int bs = block_for(V);
+    int32_t ncb = (V + bs - 1) / bs;
+    if (ncb > 1) {
+        bs = 64;
+        ncb = (V + 63) / 64;
+    }
     const int64_t total = N * ncb;
     const uint32_t grid = (uint32_t)(total < kMaxGrid ? total : kMaxGrid);
     const size_t lds = residency_lds(ncb == 1 ? kDispatchWaves : kDispatchBlocksWaves, bs);
