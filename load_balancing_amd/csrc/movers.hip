@@ -62,8 +62,11 @@ inline int block_for(int32_t V)
 // blocks at 16, the best of those (64 threads at 16: 3365 and 1552; at 32:
 // 3600 and 1910).  Rows of one block (H = 2048) stay one 256-thread
 // workgroup: 228-234 us against 239-249 for 64- or 128-thread blocks.
+// combine_bwd of rows longer than one workgroup (each thread looping over
+// several vectors) does better at 12: 3252-3294 us against 3388 at 16 on the
+// adversarial shape (H = 4096), no change on the DeepSeek-V3-like one.
 constexpr int kDispatchWaves = 12, kDispatchBlocksWaves = 24, kCombineWaves = 12,
-              kCombineBwdWaves = 16, kDispatchBwdWaves = 12;
+              kCombineBwdWaves = 16, kCombineBwdLongWaves = 12, kDispatchBwdWaves = 12;
 
 // Dynamic LDS a workgroup of `threads` requests so that only
 // waves_per_cu / (threads / 64) of them fit in one CU's LDS; the kernels do not
@@ -442,7 +445,7 @@ void run_combine_bwd(dim3 g, dim3 b, hipStream_t st, const u32x4 *dy, const u32x
                      const float *gates, const int32_t *so, u32x4 *d_out, float *d_gates,
                      int64_t total, int64_t tok0, int32_t V, int32_t K, uint32_t nrows)
 {
-    const size_t lds = residency_lds(kCombineBwdWaves, (int)b.x);
+    const size_t lds = residency_lds(V > (int32_t)b.x ? kCombineBwdLongWaves : kCombineBwdWaves, (int)b.x);
     if (tok0 == 0 && g.x == total)
         hipLaunchKernelGGL((combine_bwd_kernel<KT, false>), g, b, lds, st, dy, out, gates, so, d_out,
                            d_gates, tok0, V, K, nrows);
