@@ -515,12 +515,12 @@ int launch_dispatch_bwd(const moonep_shape &s, const uint16_t *d_buf, const int3
         return MOONEP_OK;
     const int32_t V = s.H / 8;
     const uint32_t nrows = (uint32_t)(N * s.K);
-    int bs = block_for(V);                  // block sizes as combine (2.74-2.81 ms against
-    int32_t ncb = (V + bs - 1) / bs;        // 2.83-2.87 on the DeepSeek-V3-like shape)
-    if (ncb > 1) {
-        bs = 64;
-        ncb = (V + 63) / 64;
-    }
+    // 64-thread column blocks for every row length: on the sweep's 2048-wide
+    // rows 196-198 us against 204-205 with one 256-thread workgroup per row
+    // (combine is not faster so); on the DeepSeek-V3-like shape 2.74-2.81 ms
+    // against 2.83-2.87 with 128-thread blocks
+    const int bs = 64;
+    const int32_t ncb = (V + 63) / 64;
     const int32_t cpb = ncb < 4 ? ncb : 1;  // column blocks per workgroup, as combine
     const int32_t nwb = (ncb + cpb - 1) / cpb;
     const int64_t total = N * nwb;
