@@ -63,6 +63,28 @@ def test_sizes_depend_on_shape_only(L):
     assert ws % 256 == 0 and ws >= 256 + 256 * 4
 
 
+def test_workspace_holds_the_wave_segments(L):
+    """The workspace is a 256-byte control block plus E * nseg int32 counts,
+    rounded up to 256 bytes.  Entries are cut into segments whose width is a
+    multiple of 64 entries; the count aims at NK/512 within [1024, 2048], so
+    the sweep's 262,144 entries take 1024 segments of 256 and the
+    1M-entry shapes 2048 of 512."""
+    cases = [
+        # (R, E, S, K, expected nseg)
+        (8, 64, 4096, 8, 1024),      # 262,144 entries: 256 each
+        (32, 256, 4096, 8, 2048),    # 1,048,576: 512 each
+        (16, 128, 8192, 8, 2048),    # 1,048,576
+        (4, 16, 128, 2, 16),         # 1,024 entries: the 64-entry floor
+        (8, 64, 1000, 8, 1000),      # 64,000: 64 each
+        (16, 64, 9500, 8, 1900),     # 1,216,000: 640 each
+        (4, 16, 0, 2, 0),            # empty
+    ]
+    for R, E, S, K, nseg in cases:
+        s = mx.Shape(R, E, S, K, 64)
+        want = 256 + (E * nseg * 4 + 255) // 256 * 256
+        assert mx.moonep_workspace_bytes(s) == want, (R, E, S, K)
+
+
 def test_host_errors_before_any_launch(L):
     s = mx.Shape(4, 16, 128, 2, 64)
     vp = ctypes.c_void_p
