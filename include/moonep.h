@@ -174,9 +174,11 @@ int moonep_dispatch(const moonep_shape *shape, const uint16_t *x, const int32_t 
  * Combine, the fused weighted unpermute [NCIJ three-property list and
  * explainer "pillars" panel].  expert_out: bf16 [R*S*K, H] rows in buffer
  * order (may be the dispatch buffer itself); gates: fp32 [R*S*K].
- * y[t] = bf16(sum over k ascending of gates[t*K+k] * expert_out[slot_of[t*K+k]])
- * accumulated in fp32 with fused multiply-adds, one round-to-nearest-even
- * at the end.  y: bf16 [R*S, H], must not overlap expert_out.
+ * y[t] = bf16(sum over k ascending of gates[t*K+k] * expert_out[slot_of[t*K+k]]).
+ * Each fp32 x bf16 product is exact in fp64; the products are summed in fp64
+ * in ascending k from +0 and the sum is rounded once to bf16 (to nearest
+ * even), for terms of any sign.  Out-of-range slots contribute nothing.
+ * y: bf16 [R*S, H], must not overlap expert_out.
  */
 int moonep_combine(const moonep_shape *shape, const uint16_t *expert_out, const float *gates,
                    const int32_t *slot_of, uint16_t *y, void *stream);

@@ -193,8 +193,11 @@ __global__ __launch_bounds__(kBlock) void dispatch_blocks_kernel(const u32x4 *__
     }
 }
 
-// y[t] = bf16(sum_k g * out[slot]) with an fp32 fused multiply-add chain in
-// ascending k, starting from +0; out-of-range slots contribute nothing.
+// y[t] = bf16(sum_k g * out[slot]).  Each product of an fp32 gate and a bf16
+// row element has at most 24 + 8 significant bits, so it is exact in fp64;
+// the products are summed in fp64 in ascending k from +0 and the sum is
+// rounded once to bf16 (bf16_of_double), whatever the signs of the terms.
+// Out-of-range slots contribute nothing.
 // Workgroup w = t*nwb + c covers column blocks [c*cpb, (c+1)*cpb) of token t:
 // a whole row per workgroup when it is short (under 4 column blocks), one
 // column block per workgroup otherwise; both measured best in their range.
@@ -227,10 +230,10 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const u32x4 *__restrict
              v += (int32_t)blockDim.x) {
             const int32_t *so = slot_of + (int64_t)tok * K;
             const float *gt = gates + (int64_t)tok * K;
-            float acc[8];
+            double acc[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                acc[j] = 0.0f;
+                acc[j] = 0.0;
             for (int32_t k0 = 0; k0 < K; k0 += kN) {
                 Slots<KT> sl;
                 sl.load(so, gt, K, k0, nrows, true);
@@ -238,22 +241,27 @@ __global__ __launch_bounds__(kBlock) void combine_kernel(const u32x4 *__restrict
 #pragma unroll
                 for (int c = 0; c < kN; ++c)
                     o[c] = load_nt(out + (int64_t)(sl.s[c] != 0xFFFFFFFFu ? sl.s[c] : 0u) * V + v);
+                // An out-of-range slot's row (read from row 0) and gate are
+                // replaced by zeros: its term is then fma(0, 0, acc) = acc
+                // (acc is never -0), which costs five selects per row rather
+                // than a select per accumulator update.  The products are
+                // exact, so the fused form rounds only the sum.
 #pragma unroll
                 for (int c = 0; c < kN; ++c) {
                     const bool use = sl.s[c] != 0xFFFFFFFFu;
+                    const double g = (double)(use ? sl.g[c] : 0.0f);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
-                        const float a0 = __builtin_fmaf(sl.g[c], bf16_lo(o[c][j]), acc[2 * j]);
-                        const float a1 = __builtin_fmaf(sl.g[c], bf16_hi(o[c][j]), acc[2 * j + 1]);
-                        acc[2 * j] = use ? a0 : acc[2 * j];
-                        acc[2 * j + 1] = use ? a1 : acc[2 * j + 1];
+                        const uint32_t ow = use ? o[c][j] : 0u;
+                        acc[2 * j] = __builtin_fma(g, (double)bf16_lo(ow), acc[2 * j]);
+                        acc[2 * j + 1] = __builtin_fma(g, (double)bf16_hi(ow), acc[2 * j + 1]);
                     }
                 }
             }
             u32x4 r;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                r[j] = pack_bf16(acc[2 * j], acc[2 * j + 1]);
+                r[j] = bf16_of_double(acc[2 * j]) | (bf16_of_double(acc[2 * j + 1]) << 16);
             store_nt(y + (int64_t)tok * V + v, r);
         }
     }

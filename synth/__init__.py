@@ -23,20 +23,24 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "synth.c")
-_LIB = os.path.join(_HERE, "libsynth.so")
+_BUILT = os.path.join(_HERE, "libsynth.so")
+# A sanitizer build may be loaded instead, by the sanitizer test only.
+_LIB = os.environ.get("MOONEP_SYNTH_LIB") or _BUILT
 
 # Stream tags (xor-ed into the per-seed key).
 TAG_PERM, TAG_ROUTE, TAG_LOGIT, TAG_X, TAG_DY, TAG_GRAD_REP, TAG_GRAD_HOME = 1, 2, 3, 4, 5, 6, 7
 TAG_WEIGHT = 8  # expert weights (bf16 N(0,1)), for the prefetch
+TAG_EXPERT_OUT = 9  # signed expert-output rows (bf16 N(0,1)), for combine
+TAG_SIGNED_GATE = 10  # signed fp32 N(0,1) gates, for combine under cancellation
 
 
 def build(verbose: bool = False) -> str:
     """Compile libsynth.so with gcc (OpenMP; results do not depend on threads)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", _SRC, "-o", _LIB, "-lm"]
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", _SRC, "-o", _BUILT, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.run(cmd, check=True)
-    return _LIB
+    return _BUILT
 
 
 _lib = None

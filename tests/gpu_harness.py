@@ -55,9 +55,47 @@ def stand_in_expert(topk_dev, src_of_slot_dev, scale_dev, buf, rows_per_chunk=1 
     return out
 
 
-def oracle_plan(w, topk):
+def bf16_f64(b: np.ndarray) -> np.ndarray:
+    """bf16 bits -> float64 values."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_gate_grads(g_gpu, o_dg, dy, out, slot_of, K, chunk=8192):
+    """Gate gradients within the componentwise bound, for every entry n:
+    |gpu - oracle| <= 1e-5 * sum_h |dy[n div K, h] * out[slot_of[n], h]|
+    (dy [N, H] and out [R*S*K, H] as bf16 bits; out indexed by buffer row)."""
+    g = np.asarray(g_gpu, dtype=np.float64)
+    o = np.asarray(o_dg, dtype=np.float64)
+    for n0 in range(0, slot_of.size, chunk):
+        n1 = min(slot_of.size, n0 + chunk)
+        l1 = np.abs(bf16_f64(dy[np.arange(n0, n1) // K]) * bf16_f64(out[slot_of[n0:n1]])).sum(1)
+        err = np.abs(g[n0:n1] - o[n0:n1])
+        bad = np.nonzero(err > 1e-5 * l1 + 1e-30)[0]
+        assert bad.size == 0, f"gate grad of entry {n0 + bad[0]}: err {err[bad[0]]}, l1 {l1[bad[0]]}"
+
+
+def signed_combine_inputs(w, seed, slot_of):
+    """Combine inputs with terms of both signs, as a real expert's outputs have.
+    Returns (rows, rows_cancel, gates_cancel): `rows` are N(0,1) bf16 expert
+    rows (to go with the workload's own softmax gates); `rows_cancel` repeat
+    them except that, for every token with K >= 2, the row of its second entry
+    repeats its first, and `gates_cancel` are signed N(0,1) gates with the
+    second gate -(1 + 2^-20) times the first, so the two leading terms cancel to
+    about a millionth of either."""
+    eo = synth.normal_bf16(seed, synth.TAG_EXPERT_OUT, w.NK * w.H).reshape(w.NK, w.H)
+    g_c = synth.normal_f32(seed, synth.TAG_SIGNED_GATE, w.NK)
+    eo_c = eo.copy()
+    if w.K >= 2 and w.NK:
+        n0 = np.arange(0, w.NK, w.K)
+        n1 = n0 + 1
+        eo_c[slot_of[n1]] = eo_c[slot_of[n0]]
+        g_c[n1] = (-g_c[n0].astype(np.float64) * (1.0 + 2.0 ** -20)).astype(np.float32)
+    return eo, eo_c, g_c
+
+
+def oracle_plan(w, topk, policy=oracle.PLAN_LOWEST_ID):
     T, mv = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
-    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T, policy)
     slot_of, src_of_slot = oracle.slots(w.R, w.E, w.S, w.K, topk, pl)
     return T, mv, pl, slot_of, src_of_slot
 

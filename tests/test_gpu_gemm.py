@@ -42,7 +42,7 @@ def setup(w, seed, B):
     torch.cuda.synchronize()
     o_ws = oracle.weight_slots(w.R, w.E, B, pl)
     np.testing.assert_array_equal(ws.cpu().numpy(), o_ws)
-    return s, b, pl, ws, o_ws
+    return s, b, pl, ws, o_ws, slot_of, src_of_slot
 
 
 def run_gemm(s, b, ws, B, kin, kout, x, w_home, pool, stride, off):
@@ -104,7 +104,7 @@ def test_gemm_integer_inputs_bit_exact(case):
     L = w.E // w.R
     for B in sorted({0, 1, L}):
         print(f"[case] {w.name} kin={kin} kout={kout} B={B}", flush=True)
-        s, b, pl, ws, o_ws = setup(w, 0, B)
+        s, b, pl, ws, o_ws, slot_of, _ = setup(w, 0, B)
         off = 8 * 3
         stride = off + kout * kin + 16
         w_home = bf16_of(rng.integers(-4, 5, (w.E, stride)))
@@ -114,6 +114,14 @@ def test_gemm_integer_inputs_bit_exact(case):
         want = oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, o_ws, kin, kout, x, w_home, pool,
                                   stride, off)
         np.testing.assert_array_equal(bits(y), want)
+        # the projection's signed rows combined with the workload's gates (rows
+        # of width out_dim): bit-exact against the oracle's chain
+        _, gates = synth.routing(w, 0)
+        s_out = mx.Shape(w.R, w.E, w.S, w.K, kout)
+        y_c = torch.empty((w.N, kout), dtype=torch.bfloat16, device="cuda")
+        mx.moonep_combine(s_out, y, to_dev(gates), b.slot_of, y_c)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(bits(y_c), oracle.combine(w.K, kout, want, gates, slot_of))
 
 
 @pytest.mark.parametrize("case", SMALL[:3], ids=lambda c: c[0].name)
@@ -121,7 +129,7 @@ def test_gemm_real_inputs_within_bound(case):
     w, kin, kout = case
     B = 1
     print(f"[case] {w.name} real kin={kin} kout={kout}", flush=True)
-    s, b, pl, ws, o_ws = setup(w, 1, B)
+    s, b, pl, ws, o_ws, _, _ = setup(w, 1, B)
     stride = kout * kin
     w_home = synth.expert_weights(w.E, stride * 2, 1).view(np.uint16)
     pool = synth.expert_weights(w.R * B, stride * 2, 2).view(np.uint16)
@@ -136,34 +144,46 @@ def test_gemm_real_inputs_within_bound(case):
 def full_size(w, kin, kout, off, seed, nsample, single=False, B=None):
     """The dispatch buffer of the workload times its experts' weights (rows of
     gate, up, down: 3 * H * F bf16, or one projection if single), checked on
-    sampled rows; B prefetch slots per rank (training E/R by default)."""
+    sampled rows; B prefetch slots per rank (training E/R by default).  The
+    oracle's operands come from the host inputs alone: the sampled buffer rows
+    from oracle.dispatch_rows and the pool from oracle.prefetch_weights; the
+    GPU's buffer rows and slotted pool rows are compared with those first."""
     B = w.E // w.R if B is None else B
-    s, b, pl, ws, o_ws = setup(w, seed, B)
+    s, b, pl, ws, o_ws, _, src_of_slot = setup(w, seed, B)
     H, F = w.H, kout if off == 0 else kin
     stride = kin * kout if single else 3 * H * F
     rng = np.random.default_rng(seed)
+    rows = np.unique(np.concatenate([rng.integers(0, w.NK, nsample), [0, w.NK - 1],
+                                     np.arange(w.C - 1, w.NK, w.C)]))
+    rows_d = torch.from_numpy(rows).cuda()
     w_home_np = synth.expert_weights(w.E, stride * 2, seed).view(np.uint16)
     d_home = to_dev(w_home_np.view(np.int16))
     pool = torch.empty((w.R * B, stride), dtype=torch.int16, device="cuda")
     mx.moonep_prefetch_weights(s, b.plan, ws, B, stride * 2, d_home, pool)
+    o_pool = oracle.prefetch_weights(pl, o_ws, w_home_np.view(np.uint8),
+                                     np.zeros((w.R * B, stride * 2), np.uint8)).view(np.uint16)
+    for q in sorted(int(v) for v in o_ws[:pl.n_rep] if v >= 0):
+        assert torch.equal(pool[q], to_dev(o_pool[q].view(np.int16))), f"pool slot {q}"
     if kin == H:
-        mx.moonep_dispatch(s, bf16_dev(synth.activations(w, seed)), b.slot_of, b.buf)
+        x = synth.activations(w, seed)
+        mx.moonep_dispatch(s, bf16_dev(x), b.slot_of, b.buf)
         xin = b.buf
+        x_rows = oracle.dispatch_rows(w.K, H, x, src_of_slot, rows)
+        del x
+        np.testing.assert_array_equal(bits(xin[rows_d]), x_rows)
     else:
-        xin = bf16_dev(synth.normal_bf16(seed, synth.TAG_DY, w.NK * kin).reshape(w.NK, kin))
+        x_full = synth.normal_bf16(seed, synth.TAG_DY, w.NK * kin).reshape(w.NK, kin)
+        xin = bf16_dev(x_full)
+        x_rows = x_full[rows]
+        del x_full
     y = torch.empty((w.NK, kout), dtype=torch.bfloat16, device="cuda")
     y.view(torch.int16).fill_(-1)
     mx.moonep_expert_gemm(s, b.plan, ws, B, kin, kout, xin, d_home, pool, stride, off, y)
     torch.cuda.synchronize()
     assert not (y.view(torch.int16) == -1).all(1).any(), "an output row was not written"
-    rows = np.unique(np.concatenate([rng.integers(0, w.NK, nsample), [0, w.NK - 1],
-                                     np.arange(w.C - 1, w.NK, w.C)]))
-    rows_d = torch.from_numpy(rows).cuda()
-    x_rows = bits(xin[rows_d])
-    pool_np = bits(pool.view(torch.bfloat16))
-    want = oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, o_ws, kin, kout, x_rows, w_home_np, pool_np,
+    want = oracle.expert_gemm(w.R, w.E, w.S, w.K, pl, o_ws, kin, kout, x_rows, w_home_np, o_pool,
                               stride, off, rows=rows, x_compact=True)
-    A = abs_products(w, pl, o_ws, rows, x_rows, w_home_np, pool_np, off, kin, kout)
+    A = abs_products(w, pl, o_ws, rows, x_rows, w_home_np, o_pool, off, kin, kout)
     exact = check_bound(bits(y[rows_d]), want, A, kin)
     print(f"[{w.name}] kin={kin} kout={kout} rows={rows.size} equal to the oracle: {exact:.4f}")
 

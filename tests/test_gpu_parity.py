@@ -6,7 +6,8 @@ backward, dispatch_bwd, replica_grad_reduce) and compares every output with
 the CPU oracle:
   counts, maxvio, plan, slot maps, dispatch buffer, d_out, dx, replica grads:
   bit-exact;
-  combine output: within 1 bf16 ulp (fp32 accumulation against the fp64 oracle);
+  combine output: bit-exact (both sum the exact products in fp64 in ascending k
+  and round once), also on signed expert rows and signed, cancelling gates;
   gate gradients: |gpu - oracle| <= 1e-5 * sum_h |dy_h * out_h|.
 """
 from dataclasses import replace
@@ -18,8 +19,8 @@ import torch
 import load_balancing_amd as mx
 import oracle
 import synth
-from gpu_harness import (bf16_dev, bits, compare_plan, oracle_plan, shape_of, stand_in_expert,
-                         to_dev, ulp_diff)
+from gpu_harness import (bf16_dev, bits, compare_plan, oracle_plan, shape_of,
+                         signed_combine_inputs, stand_in_expert, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -74,6 +75,12 @@ def run_and_compare(w, seed, topk=None, gates=None, G=None):
     d_home = to_dev(home)
     d_rep = to_dev(rep)
     mx.moonep_replica_grad_reduce(s, b.plan, G, d_home, d_rep)
+    # combine again on signed expert rows, and on rows whose leading terms cancel
+    eo, eo_c, sg_c = signed_combine_inputs(w, seed, slot_of)
+    y_s = torch.empty_like(y)
+    mx.moonep_combine(s, bf16_dev(eo), d_gates, b.slot_of, y_s)
+    y_c = torch.empty_like(y)
+    mx.moonep_combine(s, bf16_dev(eo_c), to_dev(sg_c), b.slot_of, y_c)
     torch.cuda.synchronize()
     assert mx.moonep_read_error(b.workspace) == mx.DEV_OK
 
@@ -85,9 +92,9 @@ def run_and_compare(w, seed, topk=None, gates=None, G=None):
     np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot)
     np.testing.assert_array_equal(bits(b.buf), o_buf)
     np.testing.assert_array_equal(bits(out), o_out)
-    y_b = bits(y)
-    du = ulp_diff(y_b, o_y)
-    assert du.max(initial=0) <= 1, f"combine off by {du.max()} ulp"
+    np.testing.assert_array_equal(bits(y), o_y)
+    np.testing.assert_array_equal(bits(y_s), oracle.combine(w.K, w.H, eo, gates, slot_of))
+    np.testing.assert_array_equal(bits(y_c), oracle.combine(w.K, w.H, eo_c, sg_c, slot_of))
     np.testing.assert_array_equal(bits(d_out), o_dout)
     g_gpu = d_g.cpu().numpy().astype(np.float64)
     if w.NK:
@@ -98,7 +105,7 @@ def run_and_compare(w, seed, topk=None, gates=None, G=None):
     np.testing.assert_array_equal(bits(dx), o_dx)
     np.testing.assert_array_equal(d_home.cpu().numpy(), o_home)
     np.testing.assert_array_equal(d_rep.cpu().numpy(), o_rep)
-    return {"exact_y": float((du == 0).mean()) if du.size else 1.0, "n_rep": pl.n_rep}
+    return {"n_rep": pl.n_rep}
 
 
 def test_tiny_config_full_chain():
