@@ -161,6 +161,25 @@ int moonep_plan(const moonep_shape *shape, const int32_t *topk_idx, const int32_
                 int32_t *src_of_slot, void *stream);
 
 /*
+ * The same plan and slot maps with fewer replicas [NCIJ three-property list:
+ * a "near-optimal" planning kernel; the pages give no algorithm].  Identical
+ * to moonep_plan (arguments, layouts, errors, and the route_stats call that
+ * must precede it) except for which entries an overfull rank gives up: it
+ * takes whole-expert amounts starting at its LARGEST expert count (ties to the
+ * lower expert id) rather than its lowest id, which sheds the excess through
+ * the fewest experts.  Each spilling expert is one entry of the spill list
+ * that the two-pointer walk matches, so the plan needs fewer replicas: 32
+ * instead of 61 on a DeepSeek-V3-like routing (R = 32, E = 256, Zipf 1.2),
+ * each replica being one expert's weights to prefetch and one gradient to
+ * reduce.  Entry order is as in moonep_plan: an expert's first keep_e
+ * entries stay home, the rest fill its replicas in plan order.
+ */
+int moonep_plan_largest_first(const moonep_shape *shape, const int32_t *topk_idx,
+                              const int32_t *expert_counts, void *workspace,
+                              size_t workspace_bytes, int32_t *plan, int32_t *slot_of,
+                              int32_t *src_of_slot, void *stream);
+
+/*
  * Dispatch, the fused permute [NCIJ three-property list, zero copy; AIPDB].
  * x: bf16 [R*S, H] token rows.  buf: bf16 [R*S*K, H], the R static [S*K, H]
  * per-rank buffers [NCIJ explainer "invariant" panel] back to back.

@@ -31,7 +31,7 @@ EXPORTS = ("moonep_check_shape", "moonep_workspace_bytes", "moonep_plan_layout_o
            "moonep_plan_bytes", "moonep_route_stats", "moonep_plan", "moonep_dispatch",
            "moonep_combine", "moonep_combine_bwd", "moonep_dispatch_bwd",
            "moonep_replica_grad_reduce", "moonep_weight_slots", "moonep_prefetch_weights",
-           "moonep_expert_gemm", "moonep_read_error")
+           "moonep_expert_gemm", "moonep_read_error", "moonep_plan_largest_first")
 
 
 class MoonepError(RuntimeError):
@@ -86,6 +86,7 @@ def lib():
             "moonep_plan_bytes": (SZ, [P]),
             "moonep_route_stats": (ctypes.c_int, [P, VP, VP, VP, VP, SZ, VP]),
             "moonep_plan": (ctypes.c_int, [P, VP, VP, VP, SZ, VP, VP, VP, VP]),
+            "moonep_plan_largest_first": (ctypes.c_int, [P, VP, VP, VP, SZ, VP, VP, VP, VP]),
             "moonep_dispatch": (ctypes.c_int, [P, VP, VP, VP, VP]),
             "moonep_combine": (ctypes.c_int, [P, VP, VP, VP, VP, VP]),
             "moonep_combine_bwd": (ctypes.c_int, [P, VP, VP, VP, VP, VP, VP, VP]),
@@ -193,6 +194,18 @@ def moonep_plan(shape, topk_idx, expert_counts, workspace, plan, slot_of, src_of
         _dev(plan, "plan", moonep_plan_bytes(shape) // 4, ("int32",)),
         _dev(slot_of, "slot_of", shape.NK, ("int32",)),
         _dev(src_of_slot, "src_of_slot", shape.NK, ("int32",)), _stream(stream)), "moonep_plan")
+
+
+def moonep_plan_largest_first(shape, topk_idx, expert_counts, workspace, plan, slot_of,
+                              src_of_slot, stream=None):
+    _check(lib().moonep_plan_largest_first(
+        ctypes.byref(shape), _dev(topk_idx, "topk_idx", shape.NK, ("int32",)),
+        _dev(expert_counts, "expert_counts", shape.E, ("int32",)),
+        _dev(workspace, "workspace", workspace.numel(), ("uint8",)), _nbytes(workspace),
+        _dev(plan, "plan", moonep_plan_bytes(shape) // 4, ("int32",)),
+        _dev(slot_of, "slot_of", shape.NK, ("int32",)),
+        _dev(src_of_slot, "src_of_slot", shape.NK, ("int32",)), _stream(stream)),
+        "moonep_plan_largest_first")
 
 
 def moonep_dispatch(shape, x, slot_of, buf, stream=None):
@@ -332,8 +345,10 @@ def allocate(shape: Shape, device="cuda") -> Buffers:
     )
 
 
-def plan_step(b: Buffers, topk_idx, stream=None):
-    """route_stats then plan: counts, maxvio, the plan and both slot maps."""
+def plan_step(b: Buffers, topk_idx, stream=None, largest_first=False):
+    """route_stats then plan (moonep_plan, or moonep_plan_largest_first):
+    counts, maxvio, the plan and both slot maps."""
     moonep_route_stats(b.shape, topk_idx, b.expert_counts, b.maxvio, b.workspace, stream)
-    moonep_plan(b.shape, topk_idx, b.expert_counts, b.workspace, b.plan, b.slot_of,
-                b.src_of_slot, stream)
+    planner = moonep_plan_largest_first if largest_first else moonep_plan
+    planner(b.shape, topk_idx, b.expert_counts, b.workspace, b.plan, b.slot_of, b.src_of_slot,
+            stream)

@@ -11,7 +11,8 @@ namespace moonep {
 int launch_route_stats(const moonep_shape &s, const int32_t *topk, int32_t *counts, float *maxvio,
                        void *ws, hipStream_t st);
 int launch_plan(const moonep_shape &s, const int32_t *topk, const int32_t *counts, void *ws,
-                int32_t *plan, int32_t *slot_of, int32_t *src_of_slot, hipStream_t st);
+                int32_t *plan, int32_t *slot_of, int32_t *src_of_slot, hipStream_t st,
+                int32_t policy);
 size_t plan_lds_bytes(int32_t E, int32_t R);
 int launch_dispatch(const moonep_shape &s, const uint16_t *x, const int32_t *slot_of, uint16_t *buf,
                     hipStream_t st);
@@ -135,9 +136,12 @@ int moonep_route_stats(const moonep_shape *shape, const int32_t *topk_idx, int32
                               (hipStream_t)stream);
 }
 
-int moonep_plan(const moonep_shape *shape, const int32_t *topk_idx, const int32_t *expert_counts,
-                void *workspace, size_t workspace_bytes, int32_t *plan, int32_t *slot_of,
-                int32_t *src_of_slot, void *stream)
+namespace {
+
+int plan_with_policy(const moonep_shape *shape, const int32_t *topk_idx,
+                     const int32_t *expert_counts, void *workspace, size_t workspace_bytes,
+                     int32_t *plan, int32_t *slot_of, int32_t *src_of_slot, void *stream,
+                     int32_t policy)
 {
     int rc = shape_status(shape);
     if (rc != MOONEP_OK)
@@ -154,7 +158,26 @@ int moonep_plan(const moonep_shape *shape, const int32_t *topk_idx, const int32_
     if (overlap(slot_of, nk * 4, src_of_slot, nk * 4))
         return MOONEP_ERR_ALIAS;
     return launch_plan(*shape, topk_idx, expert_counts, workspace, plan, slot_of, src_of_slot,
-                       (hipStream_t)stream);
+                       (hipStream_t)stream, policy);
+}
+
+}  // namespace
+
+int moonep_plan(const moonep_shape *shape, const int32_t *topk_idx, const int32_t *expert_counts,
+                void *workspace, size_t workspace_bytes, int32_t *plan, int32_t *slot_of,
+                int32_t *src_of_slot, void *stream)
+{
+    return plan_with_policy(shape, topk_idx, expert_counts, workspace, workspace_bytes, plan,
+                            slot_of, src_of_slot, stream, 0);
+}
+
+int moonep_plan_largest_first(const moonep_shape *shape, const int32_t *topk_idx,
+                              const int32_t *expert_counts, void *workspace,
+                              size_t workspace_bytes, int32_t *plan, int32_t *slot_of,
+                              int32_t *src_of_slot, void *stream)
+{
+    return plan_with_policy(shape, topk_idx, expert_counts, workspace, workspace_bytes, plan,
+                            slot_of, src_of_slot, stream, 1);
 }
 
 int moonep_dispatch(const moonep_shape *shape, const uint16_t *x, const int32_t *slot_of,

@@ -7,9 +7,11 @@
 // directly in their expert-grouped rows; the explainer's "memory" panel puts
 // prefetch (replica) rows after the home rows.  The pages give no planner, so
 // this one is the plainest greedy that meets the invariant: ranks above C
-// give up whole-expert amounts starting at their lowest expert id; these
-// amounts (in expert order) meet the deficits of the ranks below C (in rank
-// order) two-pointer; every meeting is one replica.
+// give up whole-expert amounts starting at their lowest expert id (or, in the
+// second policy, at their largest expert count, which sheds the excess
+// through the fewest experts and so needs fewer replicas); these amounts (in
+// expert order) meet the deficits of the ranks below C (in rank order)
+// two-pointer; every meeting is one replica.
 //
 // Parallel form of the two-pointer walk: with A the running totals of the
 // spill list and B those of the deficit list, the replicas are exactly the
@@ -224,9 +226,11 @@ __host__ __device__ inline int ceil_log2(int v)
     return b;
 }
 
-// The whole plan, computed by one wave into the LDS tables.
+// The whole plan, computed by one wave into the LDS tables.  policy 0: an
+// overfull rank spills from its lowest expert id; policy 1: from its largest
+// count, ties to the lower id.
 __device__ void wave_plan(const PlanLds &S, const int32_t *__restrict__ counts, int32_t R,
-                          int32_t E, int32_t C)
+                          int32_t E, int32_t C, int32_t policy)
 {
     const int lane = lane_id();
     const int32_t Lx = E / R;
@@ -252,11 +256,22 @@ __device__ void wave_plan(const PlanLds &S, const int32_t *__restrict__ counts, 
     // array: n_rep <= nA + nB - 1 <= cap - 2).  So the plan takes the same
     // time with or without replicas.
 
-    // whole-expert spill of overfull ranks, lowest expert id first
+    // whole-expert spill of overfull ranks: what the experts taken before e
+    // hold is the prefix of the rank's counts (lowest id first), or the sum of
+    // the rank's counts ordered before e by (count descending, id ascending)
+    // -- L steps for every expert, whatever the counts
     for (int e = lane; e < E; e += 64) {
         const int32_t r = e / Lx;
         const int32_t excess = S.load[r] - C;
-        const int32_t before = S.P[e] - S.P[r * Lx];
+        int32_t before = S.P[e] - S.P[r * Lx];
+        if (policy == 1) {
+            const int32_t te = S.T[e];
+            before = 0;
+            for (int32_t k = r * Lx; k < (r + 1) * Lx; ++k) {
+                const int32_t tk = S.T[k];
+                before += tk > te || (tk == te && k < e) ? tk : 0;
+            }
+        }
         int32_t give = excess - before;
         give = give < 0 ? 0 : (give > S.T[e] ? S.T[e] : give);
         give = excess > 0 ? give : 0;
@@ -381,8 +396,8 @@ __device__ void wave_plan(const PlanLds &S, const int32_t *__restrict__ counts, 
 __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
     const int32_t *__restrict__ topk, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ seg_base, int64_t nk, int32_t R, int32_t E, int32_t C,
-    int32_t segw, int32_t nseg, int32_t nbits, int32_t search_steps, int32_t *__restrict__ plan,
-    int32_t *__restrict__ slot_of, int32_t *__restrict__ src_of_slot)
+    int32_t segw, int32_t nseg, int32_t nbits, int32_t search_steps, int32_t policy,
+    int32_t *__restrict__ plan, int32_t *__restrict__ slot_of, int32_t *__restrict__ src_of_slot)
 {
     extern __shared__ int32_t lds[];
     const PlanLds S = carve(lds, E, R);
@@ -398,7 +413,7 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
         for (int e = lane; e < E; e += 64)
             run[e] = seg_base[(int64_t)e * nseg + seg];
     if (wid == 0)
-        wave_plan(S, counts, R, E, C);
+        wave_plan(S, counts, R, E, C, policy);
     __syncthreads();
 
     // ---- workgroup 0 stores the plan --------------------------------------
@@ -500,7 +515,8 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
 size_t plan_lds_bytes(int32_t E, int32_t R) { return plan_lds_words(E, R) * sizeof(int32_t); }
 
 int launch_plan(const moonep_shape &s, const int32_t *topk, const int32_t *counts, void *ws,
-                int32_t *plan, int32_t *slot_of, int32_t *src_of_slot, hipStream_t st)
+                int32_t *plan, int32_t *slot_of, int32_t *src_of_slot, hipStream_t st,
+                int32_t policy)
 {
     const WsLayout w = ws_layout(s);
     const int32_t *base = (const int32_t *)((const char *)ws + w.hist_off);
@@ -527,8 +543,8 @@ int launch_plan(const moonep_shape &s, const int32_t *topk, const int32_t *count
         }
     }
     hipLaunchKernelGGL(plan_slots_kernel, dim3(blocks), dim3(kBlock), lds, st, topk, counts, base,
-                       w.nk, s.R, s.E, s.S * s.K, w.segw, w.nseg, expert_bits(s.E), steps, plan,
-                       slot_of, src_of_slot);
+                       w.nk, s.R, s.E, s.S * s.K, w.segw, w.nseg, expert_bits(s.E), steps, policy,
+                       plan, slot_of, src_of_slot);
     return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
 }
 

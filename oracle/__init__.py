@@ -84,6 +84,8 @@ def lib():
         L.orc_route_stats.argtypes = [i32, i32, i32, i32, p, p, p]
         L.orc_plan.restype = ctypes.c_int
         L.orc_plan.argtypes = [i32, i32, i32, i32, p, ctypes.POINTER(_CPlan)]
+        L.orc_plan_policy.restype = ctypes.c_int
+        L.orc_plan_policy.argtypes = [i32, i32, i32, i32, p, i32, ctypes.POINTER(_CPlan)]
         L.orc_slots.restype = ctypes.c_int
         L.orc_slots.argtypes = [i32, i32, i32, i32, p, ctypes.POINTER(_CPlan), p, p]
         L.orc_dispatch.restype = None
@@ -170,10 +172,15 @@ def _cplan_from(plan: Plan) -> _CPlan:
     return c
 
 
-def plan(R, E, S, K, T) -> Plan:
+PLAN_LOWEST_ID, PLAN_LARGEST_FIRST = 0, 1
+
+
+def plan(R, E, S, K, T, policy=PLAN_LOWEST_ID) -> Plan:
+    """The replica plan; policy PLAN_LOWEST_ID spills an overfull rank's
+    experts from the lowest id, PLAN_LARGEST_FIRST from the largest count."""
     T = _c(T, np.int32)
     c, arrays = _alloc_plan(E, R)
-    _check(lib().orc_plan(R, E, S, K, _p(T), ctypes.byref(c)), "plan")
+    _check(lib().orc_plan_policy(R, E, S, K, _p(T), int(policy), ctypes.byref(c)), "plan")
     return Plan(c.n_rep, c.n_spill, c.n_deficit, c.max_rep_rank, arrays)
 
 

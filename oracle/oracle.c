@@ -152,8 +152,21 @@ typedef struct {
     int32_t *load, *rank_rep_first, *rank_rep_cnt;
 } orc_plan_t;
 
-int orc_plan(int32_t R, int32_t E, int32_t S, int32_t K, const int32_t *T, orc_plan_t *p)
+/*
+ * policy 0 (the plain reading of "spill in expert order"): an overfull rank
+ * gives up whole-expert amounts starting at its lowest expert id.
+ * policy 1 (the "near-optimal" planner of the three-property list, in the
+ * plainest form that needs fewer replicas): it gives them up starting at its
+ * largest expert count, ties to the lower id.  Taking the largest counts
+ * first sheds the excess through the fewest experts, and every spilling
+ * expert adds one entry to the spill list that the two-pointer walk matches.
+ * Everything after the spill amounts is the same for both.
+ */
+int orc_plan_policy(int32_t R, int32_t E, int32_t S, int32_t K, const int32_t *T, int32_t policy,
+                    orc_plan_t *p)
 {
+    if (policy != 0 && policy != 1)
+        return ORC_ERR_SHAPE;
     if (!shape_ok(R, E, S, K))
         return ORC_ERR_SHAPE;
     const int32_t L = E / R;
@@ -176,13 +189,32 @@ int orc_plan(int32_t R, int32_t E, int32_t S, int32_t K, const int32_t *T, orc_p
         p->load[r] = (int32_t)s;
     }
 
-    /* Overfull ranks give up whole-expert amounts, lowest expert id first. */
+    /* Overfull ranks give up whole-expert amounts, lowest expert id first
+       (policy 0) or largest count first (policy 1). */
     for (int32_t r = 0; r < R; ++r) {
         int32_t excess = p->load[r] > C ? p->load[r] - C : 0;
-        for (int32_t e = r * L; e < (r + 1) * L; ++e) {
-            const int32_t give = T[e] < excess ? T[e] : excess;
-            p->spill[e] = give;
-            excess -= give;
+        if (policy == 0) {
+            for (int32_t e = r * L; e < (r + 1) * L; ++e) {
+                const int32_t give = T[e] < excess ? T[e] : excess;
+                p->spill[e] = give;
+                excess -= give;
+            }
+        } else {
+            for (int32_t e = r * L; e < (r + 1) * L; ++e)
+                p->spill[e] = 0;
+            while (excess > 0) {
+                /* the largest count not yet taken; the ascending scan keeps
+                   the lowest id among equal counts */
+                int32_t best = -1;
+                for (int32_t e = r * L; e < (r + 1) * L; ++e)
+                    if (p->spill[e] == 0 && T[e] > 0 && (best < 0 || T[e] > T[best]))
+                        best = e;
+                if (best < 0)
+                    return ORC_ERR_INTERNAL;
+                const int32_t give = T[best] < excess ? T[best] : excess;
+                p->spill[best] = give;
+                excess -= give;
+            }
         }
     }
     for (int32_t e = 0; e < E; ++e)
@@ -277,6 +309,11 @@ int orc_plan(int32_t R, int32_t E, int32_t S, int32_t K, const int32_t *T, orc_p
         p->rep_cnt[e] += 1;
     }
     return ORC_OK;
+}
+
+int orc_plan(int32_t R, int32_t E, int32_t S, int32_t K, const int32_t *T, orc_plan_t *p)
+{
+    return orc_plan_policy(R, E, S, K, T, 0, p);
 }
 
 /* ------------------------------------------------------------------------ */

@@ -146,6 +146,31 @@ def test_sweep_level_full(seed, level):
     np.testing.assert_array_equal(bits(dx), oracle.dispatch_bwd(w.K, w.H, o_dbuf, slot_of))
 
 
+@pytest.mark.parametrize("name", ["dsv3", "adversarial", "sweep_mv4"])
+def test_plan_largest_first_full(name):
+    """moonep_plan_largest_first at full size: counts, maxvio, every plan
+    field and both slot maps against the oracle, and fewer replicas than the
+    lowest-id plan where the routing allows (61 -> 32 on the DeepSeek-V3-like
+    routing)."""
+    w = synth.sweep_workload(4.0, 0) if name == "sweep_mv4" else synth.WORKLOADS[name]
+    print(f"[case] {w.name} largest first", flush=True)
+    topk, _ = synth.routing(w, 0)
+    T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk, oracle.PLAN_LARGEST_FIRST)
+    s = shape_of(w)
+    b = mx.allocate(s)
+    mx.plan_step(b, to_dev(topk), largest_first=True)
+    torch.cuda.synchronize()
+    assert mx.moonep_read_error(b.workspace) == mx.DEV_OK
+    np.testing.assert_array_equal(b.expert_counts.cpu().numpy(), T)
+    assert b.maxvio.item() == mv
+    compare_plan(b.plan_fields(), pl, w.E, w.R)
+    np.testing.assert_array_equal(b.slot_of.cpu().numpy(), slot_of)
+    np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot)
+    lowest = oracle.plan(w.R, w.E, w.S, w.K, T)
+    assert pl.n_rep <= lowest.n_rep
+    print(f"[{w.name}] replicas: largest first {pl.n_rep}, lowest id {lowest.n_rep}")
+
+
 def test_dsv3_forward_sampled():
     w = synth.WORKLOADS["dsv3"]
     print(f"[case] {w.name}", flush=True)

@@ -29,8 +29,8 @@ def bf16_f64(b):
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def run_and_compare(w, seed, topk=None, gates=None, G=None):
-    print(f"[case] {w} seed={seed}", flush=True)
+def run_and_compare(w, seed, topk=None, gates=None, G=None, largest_first=False):
+    print(f"[case] {w} seed={seed} largest_first={largest_first}", flush=True)
     if topk is None:
         topk, gates = synth.routing(w, seed)
     x = synth.activations(w, seed)
@@ -42,7 +42,8 @@ def run_and_compare(w, seed, topk=None, gates=None, G=None):
     rep = synth.normal_f32(seed, synth.TAG_GRAD_REP, cap * G, 0.01).reshape(cap, G)
 
     # ---- oracle ----------------------------------------------------------
-    T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk)
+    policy = oracle.PLAN_LARGEST_FIRST if largest_first else oracle.PLAN_LOWEST_ID
+    T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk, policy)
     o_buf = oracle.dispatch(w.K, w.H, x, slot_of)
     o_out = oracle.expert(w.H, o_buf, oracle.row_expert(topk, src_of_slot), scale)
     o_y = oracle.combine(w.K, w.H, o_out, gates, slot_of)
@@ -59,7 +60,7 @@ def run_and_compare(w, seed, topk=None, gates=None, G=None):
     d_x = bf16_dev(x)
     d_dy = bf16_dev(dy)
     b.buf.view(torch.int16).fill_(-1)                      # sentinel
-    mx.plan_step(b, d_topk)
+    mx.plan_step(b, d_topk, largest_first=largest_first)
     mx.moonep_dispatch(s, d_x, b.slot_of, b.buf)
     out = stand_in_expert(d_topk, b.src_of_slot, to_dev(scale), b.buf)
     y = torch.empty((w.N, w.H), dtype=torch.bfloat16, device="cuda")
@@ -346,9 +347,12 @@ def test_two_streams_with_own_workspaces():
                 np.testing.assert_array_equal(got, want, err_msg=f"rep {rep} layer {i}")
 
 
-def test_plan_random_shapes():
+@pytest.mark.parametrize("largest_first", [False, True], ids=["lowest_id", "largest_first"])
+def test_plan_random_shapes(largest_first):
     """Plan, counts, maxvio and slot maps on 300 random small shapes (skews
-    from uniform to one hot expert), bit-exact against the oracle."""
+    from uniform to one hot expert), bit-exact against the oracle, for both
+    planners."""
+    policy = oracle.PLAN_LARGEST_FIRST if largest_first else oracle.PLAN_LOWEST_ID
     rng = np.random.default_rng(11)
     for case in range(300):
         R = int(rng.integers(1, 17))
@@ -364,10 +368,11 @@ def test_plan_random_shapes():
         topk = np.concatenate([rng.choice(E, size=K, replace=False, p=p) for _ in range(N)]
                               ).astype(np.int32) if N else np.zeros(0, dtype=np.int32)
         w = synth.Workload(f"rand{case}", R, E, S, K, 8, "zipf")
-        T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk)
+        T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk, policy)
         s = shape_of(w)
         b = mx.allocate(s)
-        mx.plan_step(b, to_dev(topk) if N else torch.empty(0, dtype=torch.int32, device="cuda"))
+        mx.plan_step(b, to_dev(topk) if N else torch.empty(0, dtype=torch.int32, device="cuda"),
+                     largest_first=largest_first)
         torch.cuda.synchronize()
         msg = f"case {case}: R={R} E={E} S={S} K={K}"
         np.testing.assert_array_equal(b.expert_counts.cpu().numpy(), T, err_msg=msg)
@@ -376,6 +381,14 @@ def test_plan_random_shapes():
         if N:
             np.testing.assert_array_equal(b.slot_of.cpu().numpy(), slot_of, err_msg=msg)
             np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot, err_msg=msg)
+
+
+@pytest.mark.parametrize("w", [synth.WORKLOADS["tiny"]] + [e for e in EDGE if e.name in (
+    "ragged", "heavy_skew", "k9", "adversarial_small")] + LIMITS[:2], ids=lambda w: w.name)
+def test_whole_chain_largest_first(w):
+    """The element-by-element chain with the largest-first planner: its plan
+    feeds the same slot assignment, movers and reduction."""
+    run_and_compare(w, 0, largest_first=True)
 
 
 def test_whole_chain_random_shapes():

@@ -22,8 +22,12 @@ MUTANTS = {
     "maxvio_wrong_operand": ("(double)((int64_t)tmax * E)", "(double)((int64_t)tmax * R)"),
     "count_drops_last_entry": ("for (int64_t n = 0; n < NK; ++n) {\n        const int32_t e = topk[n];\n        if (e < 0 || e >= E)\n            return ORC_ERR_EXPERT_ID;",
                                "for (int64_t n = 0; n + 1 < NK; ++n) {\n        const int32_t e = topk[n];\n        if (e < 0 || e >= E)\n            return ORC_ERR_EXPERT_ID;"),
-    "spill_highest_id_first": ("for (int32_t e = r * L; e < (r + 1) * L; ++e) {\n            const int32_t give",
-                               "for (int32_t e = (r + 1) * L - 1; e >= r * L; --e) {\n            const int32_t give"),
+    "spill_highest_id_first": ("for (int32_t e = r * L; e < (r + 1) * L; ++e) {\n                const int32_t give",
+                               "for (int32_t e = (r + 1) * L - 1; e >= r * L; --e) {\n                const int32_t give"),
+    "largest_first_ties_to_higher_id": ("(best < 0 || T[e] > T[best])", "(best < 0 || T[e] >= T[best])"),
+    "largest_first_takes_smallest": ("(best < 0 || T[e] > T[best])", "(best < 0 || T[e] < T[best])"),
+    "largest_first_spills_whole_expert": ("const int32_t give = T[best] < excess ? T[best] : excess;",
+                                          "const int32_t give = T[best];"),
     "deficit_includes_full_ranks": ("if (p->load[r] < C) {\n            df_r[nd]", "if (p->load[r] <= C) {\n            df_r[nd]"),
     "spill_off_from_remainder": ("p->rep_spill_off[nrep] = sp_amt[i] - rem_s;", "p->rep_spill_off[nrep] = rem_s;"),
     "tie_advances_one_pointer": ("        if (rem_d == 0) {\n            ++j;", "        else if (rem_d == 0) {\n            ++j;"),

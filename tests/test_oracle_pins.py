@@ -63,20 +63,30 @@ def torch_bf16_bits(f32: np.ndarray) -> np.ndarray:
     return t.view(torch.int16).numpy().view(np.uint16)
 
 
-def union_intervals_plan(T, R, E, S, K):
+def spill_amounts(T, R, E, C, policy=0):
+    """Entries each expert gives up, by sorting each overfull rank's experts
+    (not the oracle's scan): ascending id (policy 0), or count descending
+    with ties to the lower id (policy 1); each takes min(count, what is left)."""
+    L = E // R
+    sp = [0] * E
+    for r in range(R):
+        x = max(sum(T[r * L:(r + 1) * L]) - C, 0)
+        order = list(range(r * L, (r + 1) * L))
+        if policy == 1:
+            order.sort(key=lambda e: (-T[e], e))
+        for e in order:
+            sp[e] = min(T[e], x)
+            x -= sp[e]
+    return sp
+
+
+def union_intervals_plan(T, R, E, S, K, policy=0):
     """Replicas as the intervals between consecutive values of the union of the
     cumulative spill totals and the cumulative deficit totals (a merge, not a
-    two-pointer walk).  Spill amounts follow the lowest-id-first reading."""
+    two-pointer walk), for the spill amounts of either policy."""
     L, C = E // R, S * K
     load = [sum(T[r * L:(r + 1) * L]) for r in range(R)]
-    spill = []
-    for r in range(R):
-        x = max(load[r] - C, 0)
-        for e in range(r * L, (r + 1) * L):
-            g = min(T[e], x)
-            x -= g
-            if g:
-                spill.append((e, g))
+    spill = [(e, g) for e, g in enumerate(spill_amounts(T, R, E, C, policy)) if g]
     deficit = [(r, C - load[r]) for r in range(R) if load[r] < C]
     A = list(itertools.accumulate(a for _, a in spill))
     B = list(itertools.accumulate(b for _, b in deficit))
@@ -148,7 +158,7 @@ def brute_min_replicas(T, R, E, C):
     raise AssertionError("infeasible")
 
 
-def check_plan_invariants(T, pl, R, E, S, K):
+def check_plan_invariants(T, pl, R, E, S, K, policy=0):
     L, C = E // R, S * K
     T = np.asarray(T)
     n = pl.n_rep
@@ -172,17 +182,30 @@ def check_plan_invariants(T, pl, R, E, S, K):
     assert (n == 0) == bool((load == C).all())
     # the two-pointer bound
     assert n <= max(pl.n_spill + pl.n_deficit - 1, 0)
-    # the lowest-id-first reading: inside an overfull rank, spill is a prefix
     for r in range(R):
         sp = pl.spill[r * L:(r + 1) * L]
         te = T[r * L:(r + 1) * L]
         assert sp.sum() == max(load[r] - C, 0)
-        partial = False
-        for e in range(L):
-            if partial:
-                assert sp[e] == 0
-            elif sp[e] < te[e]:
-                partial = True
+        if policy == 0:
+            # the lowest-id-first reading: inside an overfull rank, spill is a prefix
+            partial = False
+            for e in range(L):
+                if partial:
+                    assert sp[e] == 0
+                elif sp[e] < te[e]:
+                    partial = True
+        else:
+            # largest first: the spilling experts are the fewest that cover
+            # the excess (the k largest counts, k minimal), all but the
+            # smallest of them spill whole
+            x = max(load[r] - C, 0)
+            desc = np.sort(te)[::-1]
+            kmin = int(np.searchsorted(np.cumsum(desc), x)) + 1 if x else 0
+            spilling = np.nonzero(sp)[0]
+            assert len(spilling) == kmin
+            if kmin:
+                assert te[spilling].min() >= np.delete(te, spilling).max(initial=0)
+                assert int((sp[spilling] < te[spilling]).sum()) <= 1
     # replicas of one expert and of one host are consecutive ids
     for arr in (exp_, host):
         seen = set()
@@ -281,6 +304,31 @@ def test_hand_examples(ex):
         assert (ws[pl.n_rep:] == -1).all()
 
 
+def load_largest_first_golden():
+    with open(os.path.join(GOLDEN, "largest_first_examples.json")) as f:
+        return json.load(f)["examples"]
+
+
+@pytest.mark.parametrize("ex", load_largest_first_golden(), ids=lambda ex: ex["name"])
+def test_largest_first_hand_examples(ex):
+    R, E, S, K = ex["R"], ex["E"], ex["S"], ex["K"]
+    topk = np.array(ex["topk"], dtype=np.int32)
+    T, _ = oracle.route_stats(R, E, S, K, topk)
+    assert T.tolist() == ex["T"]
+    pl = oracle.plan(R, E, S, K, T, oracle.PLAN_LARGEST_FIRST)
+    assert pl.n_rep == ex["n_rep"]
+    for j, rep in enumerate(ex["replicas"]):
+        assert (pl.rep_expert[j], pl.rep_host[j], pl.rep_count[j], pl.rep_spill_off[j],
+                pl.rep_row_off[j]) == (rep["expert"], rep["host"], rep["count"],
+                                       rep["spill_off"], rep["row_off"])
+    assert pl.keep.tolist() == ex["keep"]
+    assert pl.home_row_off.tolist() == ex["home_row_off"]
+    slot_of, src_of_slot = oracle.slots(R, E, S, K, topk, pl)
+    assert slot_of.tolist() == ex["slot_of"]
+    assert (src_of_slot[slot_of] == np.arange(len(topk))).all()
+    assert oracle.plan(R, E, S, K, T).n_rep == ex["lowest_id_n_rep"]
+
+
 def test_counts_match_bincount_and_sum():
     rng = np.random.default_rng(3)
     for _ in range(50):
@@ -333,42 +381,49 @@ def test_maxvio_edge_cases():
 # plan
 # ---------------------------------------------------------------------------
 
-def test_plan_invariants_random_tiny():
+POLICIES = [oracle.PLAN_LOWEST_ID, oracle.PLAN_LARGEST_FIRST]
+
+
+@pytest.mark.parametrize("policy", POLICIES)
+def test_plan_invariants_random_tiny(policy):
     rng = np.random.default_rng(4)
     for _ in range(2000):
         R, E, S, K, topk = random_tiny(rng)
         T, _ = oracle.route_stats(R, E, S, K, topk)
-        pl = oracle.plan(R, E, S, K, T)
-        check_plan_invariants(T, pl, R, E, S, K)
+        pl = oracle.plan(R, E, S, K, T, policy)
+        check_plan_invariants(T, pl, R, E, S, K, policy)
 
 
-def test_plan_equals_union_of_boundaries():
+@pytest.mark.parametrize("policy", POLICIES)
+def test_plan_equals_union_of_boundaries(policy):
     rng = np.random.default_rng(5)
     for _ in range(1000):
         R, E, S, K, topk = random_tiny(rng)
         T, _ = oracle.route_stats(R, E, S, K, topk)
-        pl = oracle.plan(R, E, S, K, T)
-        reps = union_intervals_plan(T.tolist(), R, E, S, K)
+        pl = oracle.plan(R, E, S, K, T, policy)
+        reps = union_intervals_plan(T.tolist(), R, E, S, K, policy)
         assert pl.n_rep == len(reps)
         got = list(zip(pl.rep_expert[:pl.n_rep].tolist(), pl.rep_host[:pl.n_rep].tolist(),
                        pl.rep_count[:pl.n_rep].tolist(), pl.rep_spill_off[:pl.n_rep].tolist()))
         assert got == reps
 
 
+@pytest.mark.parametrize("policy", POLICIES)
 @pytest.mark.parametrize("name", ["tiny", "sweep", "dsv3"])
-def test_plan_equals_union_of_boundaries_full(name):
+def test_plan_equals_union_of_boundaries_full(name, policy):
     w = synth.WORKLOADS[name]
     topk, _ = synth.routing(w, 0)
     T, _ = oracle.route_stats(w.R, w.E, w.S, w.K, topk)
-    pl = oracle.plan(w.R, w.E, w.S, w.K, T)
-    check_plan_invariants(T, pl, w.R, w.E, w.S, w.K)
-    reps = union_intervals_plan(T.tolist(), w.R, w.E, w.S, w.K)
+    pl = oracle.plan(w.R, w.E, w.S, w.K, T, policy)
+    check_plan_invariants(T, pl, w.R, w.E, w.S, w.K, policy)
+    reps = union_intervals_plan(T.tolist(), w.R, w.E, w.S, w.K, policy)
     got = list(zip(pl.rep_expert[:pl.n_rep].tolist(), pl.rep_host[:pl.n_rep].tolist(),
                    pl.rep_count[:pl.n_rep].tolist(), pl.rep_spill_off[:pl.n_rep].tolist()))
     assert got == reps
 
 
-def test_plan_never_below_brute_force_minimum():
+@pytest.mark.parametrize("policy", POLICIES)
+def test_plan_never_below_brute_force_minimum(policy):
     rng = np.random.default_rng(6)
     gaps = []
     cases = 0
@@ -384,7 +439,7 @@ def test_plan_never_below_brute_force_minimum():
         N = R * S
         topk = np.concatenate([rng.choice(E, size=K, replace=False) for _ in range(N)]).astype(np.int32)
         T, _ = oracle.route_stats(R, E, S, K, topk)
-        pl = oracle.plan(R, E, S, K, T)
+        pl = oracle.plan(R, E, S, K, T, policy)
         lo = brute_min_replicas(T.tolist(), R, E, C)
         assert pl.n_rep >= lo
         # a lower bound that any plan obeys
@@ -392,8 +447,8 @@ def test_plan_never_below_brute_force_minimum():
         assert pl.n_rep >= max(int((load > C).sum()), int((load < C).sum())) or pl.n_rep == 0
         gaps.append(pl.n_rep - lo)
         cases += 1
-    # the greedy is near the minimum on these inputs
-    assert max(gaps) <= 2
+    # the greedy is near the minimum on these inputs; largest first reaches it
+    assert max(gaps) <= (2 if policy == oracle.PLAN_LOWEST_ID else 0)
 
 
 def test_plan_adversarial_closed_form():
