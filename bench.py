@@ -120,11 +120,18 @@ def source_hash(files=MOVER_SOURCES):
     return h.hexdigest()[:16]
 
 
-def cpu_baseline(levels, seed, runs=3):
-    """The CPU oracle, single-threaded, on the forward of every maxvio level;
-    the median of `runs` passes over the levels."""
+def cpu_baseline(levels, seed, runs=3, bwd_level=4.0):
+    """The CPU oracle, single-threaded, phase by phase: the forward of every
+    maxvio level, then the backward (combine_bwd, dispatch_bwd, the replica
+    reduction) of one level; the median of `runs` passes of each."""
+    import numpy as np
+
     import oracle
     import synth
+
+    def median_pass(fn):
+        passes = sorted((fn() for _ in range(runs)), key=lambda p: sum(p.values()))
+        return passes[len(passes) // 2]
 
     inputs = []
     for level in levels:
@@ -135,9 +142,9 @@ def cpu_baseline(levels, seed, runs=3):
     for wl, *_ in inputs:
         b = algorithmic_bytes(wl.R, wl.S, wl.K, wl.H)
         dc += b["dispatch"] + b["combine"]
-    passes = []
-    for _ in range(runs):
-        t_plan = t_disp = t_comb = 0.0
+
+    def forward():
+        t = {"route_stats+plan+slots": 0.0, "dispatch": 0.0, "combine": 0.0}
         for wl, topk, gates, x in inputs:
             t0 = time.perf_counter()
             T, _ = oracle.route_stats(wl.R, wl.E, wl.S, wl.K, topk)
@@ -149,20 +156,52 @@ def cpu_baseline(levels, seed, runs=3):
             oracle.combine(wl.K, wl.H, buf, gates, slot_of)
             t3 = time.perf_counter()
             del buf
-            t_plan += t1 - t0
-            t_disp += t2 - t1
-            t_comb += t3 - t2
-        passes.append((t_disp + t_comb, t_plan, t_disp, t_comb))
-    passes.sort()
-    dc_t, t_plan, t_disp, t_comb = passes[len(passes) // 2]
+            t["route_stats+plan+slots"] += t1 - t0
+            t["dispatch"] += t2 - t1
+            t["combine"] += t3 - t2
+        return t
+
+    fwd = median_pass(forward)
+    # backward of one level: the identity expert, as in the benchmark step
+    wl, topk, gates, x = inputs[list(levels).index(bwd_level)]
+    T, _ = oracle.route_stats(wl.R, wl.E, wl.S, wl.K, topk)
+    pl = oracle.plan(wl.R, wl.E, wl.S, wl.K, T)
+    slot_of, _ = oracle.slots(wl.R, wl.E, wl.S, wl.K, topk, pl)
+    buf = oracle.dispatch(wl.K, wl.H, x, slot_of)
+    dy = synth.activations(wl, seed, synth.TAG_DY)
+    G, cap = wl.G, wl.E + wl.R
+    home = synth.normal_f32(seed, synth.TAG_GRAD_HOME, wl.E * G, 0.01).reshape(wl.E, G)
+    rep = synth.normal_f32(seed, synth.TAG_GRAD_REP, cap * G, 0.01).reshape(cap, G)
+
+    def backward():
+        t0 = time.perf_counter()
+        d_out, _ = oracle.combine_bwd(wl.K, wl.H, dy, buf, gates, slot_of)
+        t1 = time.perf_counter()
+        oracle.dispatch_bwd(wl.K, wl.H, d_out, slot_of)
+        t2 = time.perf_counter()
+        oracle.replica_grad_reduce(wl.E, pl, G, home, rep)
+        t3 = time.perf_counter()
+        return {"combine_bwd": t1 - t0, "dispatch_bwd": t2 - t1, "replica_grad_reduce": t3 - t2}
+
+    bwd = median_pass(backward)
+    bb = algorithmic_bytes(wl.R, wl.S, wl.K, wl.H, G, [int(c) for c in pl.rep_cnt])
+    gbps = {"dispatch": sum(algorithmic_bytes(w.R, w.S, w.K, w.H)["dispatch"] for w, *_ in inputs)
+                        / fwd["dispatch"] / 1e9,
+            "combine": sum(algorithmic_bytes(w.R, w.S, w.K, w.H)["combine"] for w, *_ in inputs)
+                       / fwd["combine"] / 1e9}
+    for k in bwd:
+        gbps[k] = bb[k] / bwd[k] / 1e9
     model, nproc = host_cpu()
-    return {"value": round(dc / dc_t / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "host_cpu": model, "host_nproc": nproc,
-            "sample": f"one forward step at each maxvio level {list(levels)} (seed {seed}), "
-                      f"single thread, median of {runs} passes: route_stats+plan+slots "
-                      f"{1e3 * t_plan:.1f} ms, dispatch {1e3 * t_disp:.1f} ms, combine "
-                      f"{1e3 * t_comb:.1f} ms per pass; value = dispatch+combine algorithmic "
-                      f"bytes / their time"}
+    return {"value": round(dc / (fwd["dispatch"] + fwd["combine"]) / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle", "host_cpu": model, "host_nproc": nproc,
+            "phase_ms": {k: round(1e3 * v, 1) for k, v in {**fwd, **bwd}.items()},
+            "phase_GBps": {k: round(v, 4) for k, v in gbps.items()},
+            "sample": f"single thread, median of {runs} passes per phase: the forward (route_stats, "
+                      f"plan and slots, dispatch, combine) of one step at each maxvio level "
+                      f"{list(levels)}, and the backward (combine_bwd, dispatch_bwd, the replica "
+                      f"reduction of {pl.n_rep} replicas of 2048x1408 fp32 gradients) of the "
+                      f"maxvio {bwd_level:g} step (seed {seed}); phase_ms: forward phases summed "
+                      f"over the levels; value = dispatch+combine algorithmic bytes / their time"}
 
 
 def cpu_baseline_sampled(w, seed, ntok=2048):
@@ -225,6 +264,56 @@ def plan_latency(mx, s, b, topks, levels, stream, reps=20):
         t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
         out[lv] = round(1e3 * t[reps // 2], 2)
     return out
+
+
+def seed_leg(mx, s, b, y, seed, flush, stream, reps=4):
+    """The sweep levels of another seed (its own bisected Zipf exponents,
+    tokens and gates), timed as in the steps: dispatch+combine GB/s over
+    `reps` evicted-cache passes per level, and route_stats + plan per level
+    as plan_latency times it."""
+    import numpy as np
+    import torch
+
+    import synth
+
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(b.buf.device)
+    levels, topks, gts = [], [], []
+    for lv in synth.SWEEP_LEVELS:
+        t, g = synth.routing(synth.sweep_workload(lv, seed), seed)
+        levels.append(f"{lv:g}")
+        topks.append(up(t))
+        gts.append(up(g))
+    x = up(synth.activations(synth.WORKLOADS["sweep"], seed).view(np.int16)).view(torch.bfloat16)
+    n_rep, maxvio, ev = {}, {}, []
+    for lv, tk, gt in zip(levels, topks, gts):
+        mx.moonep_route_stats(s, tk, b.expert_counts, b.maxvio, b.workspace, stream)
+        mx.moonep_plan(s, tk, b.expert_counts, b.workspace, b.plan, b.slot_of, b.src_of_slot,
+                       stream)
+        n_rep[lv] = int(b.plan_fields()["n_rep"])
+        maxvio[lv] = round(float(b.maxvio.item()), 4)
+        for _ in range(reps):
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            flush()
+            e[0].record(stream)
+            mx.moonep_dispatch(s, x, b.slot_of, b.buf, stream)
+            e[1].record(stream)
+            flush()
+            e[2].record(stream)
+            mx.moonep_combine(s, b.buf, gt, b.slot_of, y, stream)
+            e[3].record(stream)
+            ev.append(e)
+    torch.cuda.synchronize()
+    assert mx.moonep_read_error(b.workspace) == 0
+    ms = sum(e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]) for e in ev)
+    byt = algorithmic_bytes(s.R, s.S, s.K, s.H)
+    gbps = len(ev) * (byt["dispatch"] + byt["combine"]) / (1e-3 * ms) / 1e9
+    plan_us = plan_latency(mx, s, b, topks, levels, stream)
+    pv = list(plan_us.values())
+    return {"value": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+            "plan_us_vs_maxvio": plan_us, "plan_spread": round((max(pv) - min(pv)) / min(pv), 4),
+            "replicas_per_level": n_rep, "maxvio_per_level": maxvio,
+            "alpha_per_level": {f"{lv:g}": synth.sweep_alpha(seed, lv)
+                                for lv in synth.SWEEP_LEVELS if lv}}
 
 
 def gemm_traffic(workload):
@@ -298,6 +387,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="sweep", choices=("sweep", "dsv3", "adversarial", "tiny"))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-seeds", default="1,2",
+                    help="sweep only: seeds timed after the steps (dispatch+combine and plan "
+                         "per level); empty for none")
     ap.add_argument("--no-expert-gemm", action="store_true",
                     help="skip the timed grouped-GEMM leg after the steps")
     ap.add_argument("--no-copy-probe", action="store_true",
@@ -398,7 +490,7 @@ def main():
         for c, fn in enumerate(calls):
             if CALLS[c] in MOVERS:
                 flush()
-            if ev is not None:
+            if ev is not None and ev[c][0] is not (ev[c - 1][1] if c else None):
                 ev[c][0].record(stream)
             fn()
             if ev is not None:
@@ -427,8 +519,18 @@ def main():
         step(i)
     torch.cuda.synchronize()
 
-    events = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(len(CALLS))] for _ in range(args.steps)]
+    def step_events():
+        """A start and an end event per call; a call that follows the previous
+        one with no untimed eviction between them starts at that call's end
+        event, so no extra event sits between back-to-back calls."""
+        ev = []
+        for c, name in enumerate(CALLS):
+            start = (ev[c - 1][1] if c and name not in MOVERS
+                     else torch.cuda.Event(enable_timing=True))
+            ev.append((start, torch.cuda.Event(enable_timing=True)))
+        return ev
+
+    events = [step_events() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -438,12 +540,16 @@ def main():
 
     per_call = {c: [] for c in CALLS}
     per_level = {lv: {c: [] for c in CALLS} for lv in levels}
+    plan_in_step = {lv: [] for lv in levels}
+    ip = CALLS.index("plan")
     for i in range(args.steps):
         lv = levels[i % len(levels)]
         for c, name in enumerate(CALLS):
             ms = events[i][c][0].elapsed_time(events[i][c][1])
             per_call[name].append(ms)
             per_level[lv][name].append(ms)
+        # route_stats + plan as one span: the first call's start to the plan's end
+        plan_in_step[lv].append(events[i][0][0].elapsed_time(events[i][ip][1]))
     mean = lambda v: sum(v) / len(v)
     us = {c: round(1e3 * mean(v), 2) for c, v in per_call.items()}
     med = {c: round(1e3 * sorted(v)[len(v) // 2], 2) for c, v in per_call.items()}
@@ -452,9 +558,10 @@ def main():
     dc_bytes = byt["dispatch"] + byt["combine"]
     dc_s = 1e-3 * (mean(per_call["dispatch"]) + mean(per_call["combine"]))
     value = dc_bytes / dc_s / 1e9
-    plan_us_in_step = {lv: round(1e3 * (mean(per_level[lv]["route_stats"]) +
-                                        mean(per_level[lv]["plan"])), 2)
-                       for lv in levels if per_level[lv]["plan"]}
+    median = lambda v: (sorted(v)[len(v) // 2] if len(v) % 2 else
+                        0.5 * (sorted(v)[len(v) // 2 - 1] + sorted(v)[len(v) // 2]))
+    plan_us_in_step = {lv: round(1e3 * median(v), 2) for lv, v in plan_in_step.items() if v}
+    pis = list(plan_us_in_step.values())
     plan_us = plan_latency(mx, s, b, topks, levels, stream)
     pv = list(plan_us.values())
     kern = {}
@@ -517,6 +624,9 @@ def main():
         "plan_def": "route_stats + plan, median of 20 pairs per level, HIP events, each pair "
                     "queued behind a 40 us copy so no launch gap is timed",
         "plan_us_in_step": plan_us_in_step,
+        "plan_spread_in_step": round((max(pis) - min(pis)) / min(pis), 4) if pis else None,
+        "plan_in_step_def": "route_stats start event to plan end event inside the timed steps "
+                            "(no event between the two calls), median over the steps of each level",
         "breakdown_us": us,
         "breakdown_median_us": med,
         "kernels": kern,
@@ -527,6 +637,10 @@ def main():
                                             zip(levels, reps_per_level, pref_per_level)}},
         "roofline": roof,
     }
+    if args.workload == "sweep" and args.extra_seeds:
+        result["other_seeds"] = {
+            sd: seed_leg(mx, s, b, y, int(sd), flush, stream)
+            for sd in args.extra_seeds.split(",") if int(sd) != args.seed}
     if args.workload == "tiny":
         result["expert_gemm"] = {"skipped": "H = 64 is below the grouped GEMM's 128-column "
                                             "granularity"}
