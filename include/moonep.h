@@ -180,6 +180,27 @@ int moonep_plan_largest_first(const moonep_shape *shape, const int32_t *topk_idx
                               int32_t *src_of_slot, void *stream);
 
 /*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the work of
+ * moonep_route_stats followed by moonep_plan, with the workspace replaced by a
+ * scratch array inside the library, MOONEP_NOALLOC_SCRATCH_BYTES per device
+ * (enough for every valid shape), held until the process ends.  Allocates
+ * nothing.  Writes expert_counts, maxvio, plan, slot_of and src_of_slot
+ * exactly as those two calls do.  Every call on one device shares that
+ * device's scratch and leaves its contents behind (nothing in it must start
+ * at zero between calls), so calls that overlap on one device -- other
+ * streams, other host threads -- race and must be ordered by the caller.  An
+ * expert id outside [0, E) gives its entries slot_of = -1 as in moonep_plan;
+ * the scratch's error word cannot be read with moonep_read_error.  Returns
+ * MOONEP_ERR_WORKSPACE if a shape needed more scratch than the array holds,
+ * MOONEP_ERR_HIP if the scratch's device address cannot be obtained.
+ */
+enum { MOONEP_NOALLOC_SCRATCH_BYTES = 256 + 4 * 1024 * 2048 };
+int moonep_plan_noalloc(const moonep_shape *shape, const int32_t *topk_idx, int32_t *expert_counts,
+                        float *maxvio, int32_t *plan, int32_t *slot_of, int32_t *src_of_slot,
+                        void *stream);
+
+/*
  * Dispatch, the fused permute [NCIJ three-property list, zero copy; AIPDB].
  * x: bf16 [R*S, H] token rows.  buf: bf16 [R*S*K, H], the R static [S*K, H]
  * per-rank buffers [NCIJ explainer "invariant" panel] back to back.

@@ -31,7 +31,8 @@ EXPORTS = ("moonep_check_shape", "moonep_workspace_bytes", "moonep_plan_layout_o
            "moonep_plan_bytes", "moonep_route_stats", "moonep_plan", "moonep_dispatch",
            "moonep_combine", "moonep_combine_bwd", "moonep_dispatch_bwd",
            "moonep_replica_grad_reduce", "moonep_weight_slots", "moonep_prefetch_weights",
-           "moonep_expert_gemm", "moonep_read_error", "moonep_plan_largest_first")
+           "moonep_expert_gemm", "moonep_read_error", "moonep_plan_largest_first",
+           "moonep_plan_noalloc")
 
 
 class MoonepError(RuntimeError):
@@ -97,6 +98,7 @@ def lib():
             "moonep_expert_gemm": (ctypes.c_int, [P, VP, VP, ctypes.c_int32, ctypes.c_int32,
                                                   ctypes.c_int32, VP, VP, VP, I64, I64, VP, VP]),
             "moonep_read_error": (ctypes.c_int, [VP, SZ, ctypes.POINTER(ctypes.c_int32), VP]),
+            "moonep_plan_noalloc": (ctypes.c_int, [P, VP, VP, VP, VP, VP, VP, VP]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -206,6 +208,18 @@ def moonep_plan_largest_first(shape, topk_idx, expert_counts, workspace, plan, s
         _dev(slot_of, "slot_of", shape.NK, ("int32",)),
         _dev(src_of_slot, "src_of_slot", shape.NK, ("int32",)), _stream(stream)),
         "moonep_plan_largest_first")
+
+
+def moonep_plan_noalloc(shape, topk_idx, expert_counts, maxvio, plan, slot_of, src_of_slot,
+                        stream=None):
+    _check(lib().moonep_plan_noalloc(
+        ctypes.byref(shape), _dev(topk_idx, "topk_idx", shape.NK, ("int32",)),
+        _dev(expert_counts, "expert_counts", shape.E, ("int32",)),
+        _dev(maxvio, "maxvio", 1, ("float32",)),
+        _dev(plan, "plan", moonep_plan_bytes(shape) // 4, ("int32",)),
+        _dev(slot_of, "slot_of", shape.NK, ("int32",)),
+        _dev(src_of_slot, "src_of_slot", shape.NK, ("int32",)), _stream(stream)),
+        "moonep_plan_noalloc")
 
 
 def moonep_dispatch(shape, x, slot_of, buf, stream=None):

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moonep_internal.hpp"
 
 namespace moonep {
@@ -38,7 +40,37 @@ int launch_expert_gemm(const moonep_shape &s, const int32_t *plan, const int32_t
 
 using namespace moonep;
 
+// Scratch of moonep_plan_noalloc: the route_stats -> plan workspace of any
+// valid shape (the 256-byte control block plus E x nseg int32 counts, with
+// E <= 1024 and at most 2048 wave segments), one copy per device, held until
+// the process ends.  In host code this name is not a device address: the
+// address comes from hipGetSymbolAddress, once per device (static_scratch).
+constexpr size_t kStaticScratchBytes = kCtlBytes + (size_t)4 * kMaxExperts * kMaxSegments;
+static_assert(kStaticScratchBytes == (size_t)MOONEP_NOALLOC_SCRATCH_BYTES, "scratch size");
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+int static_scratch(void **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return MOONEP_ERR_HIP;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return MOONEP_ERR_HIP;
+        scratch_ptr[dev] = p;
+    }
+    *out = scratch_ptr[dev];
+    return MOONEP_OK;
+}
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -178,6 +210,33 @@ int moonep_plan_largest_first(const moonep_shape *shape, const int32_t *topk_idx
 {
     return plan_with_policy(shape, topk_idx, expert_counts, workspace, workspace_bytes, plan,
                             slot_of, src_of_slot, stream, 1);
+}
+
+int moonep_plan_noalloc(const moonep_shape *shape, const int32_t *topk_idx, int32_t *expert_counts,
+                        float *maxvio, int32_t *plan, int32_t *slot_of, int32_t *src_of_slot,
+                        void *stream)
+{
+    int rc = shape_status(shape);
+    if (rc != MOONEP_OK)
+        return rc;
+    const int64_t nk = n_entries(shape);
+    if (!present(topk_idx, nk) || !expert_counts || !maxvio || !plan || !present(slot_of, nk) ||
+        !present(src_of_slot, nk))
+        return MOONEP_ERR_NULL_PTR;
+    if (!aligned(topk_idx, 4) || !aligned(expert_counts, 4) || !aligned(maxvio, 4) ||
+        !aligned(plan, 4) || !aligned(slot_of, 4) || !aligned(src_of_slot, 4))
+        return MOONEP_ERR_MISALIGNED;
+    if (overlap(slot_of, nk * 4, src_of_slot, nk * 4))
+        return MOONEP_ERR_ALIAS;
+    if (ws_layout(*shape).bytes > kStaticScratchBytes)
+        return MOONEP_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if ((rc = static_scratch(&ws)) != MOONEP_OK)
+        return rc;
+    const hipStream_t st = (hipStream_t)stream;
+    if ((rc = launch_route_stats(*shape, topk_idx, expert_counts, maxvio, ws, st)) != MOONEP_OK)
+        return rc;
+    return launch_plan(*shape, topk_idx, expert_counts, ws, plan, slot_of, src_of_slot, st, 0);
 }
 
 int moonep_dispatch(const moonep_shape *shape, const uint16_t *x, const int32_t *slot_of,
