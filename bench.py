@@ -379,6 +379,84 @@ def expert_gemm_leg(mx, s, b, wslot, B_slots, w_home, pool, wbytes, d_out, reps,
                          "algorithmic_flops_per_launch": flops}}
 
 
+MAP_STUDY = ("identity", "plan mv0", "plan mv4", "uniform expert", "random permutation")
+
+
+def map_study(reps=5, seed=0):
+    """The four movers on the sweep shape over destination maps that are not
+    all plans, to separate what the access pattern costs from what the
+    kernels cost: the identity map (entry n -> row n, every row write and
+    read sequential), the plans of the balanced and the maxvio-4 routings,
+    a uniform random expert per entry (stable within each expert, evenly
+    loaded), and a random permutation of all rows.  Each call from an evicted
+    cache, `reps` calls per mover and map, in the order of MAP_STUDY and,
+    within a map, dispatch, combine, combine_bwd, dispatch_bwd (so a
+    kernel-trace's calls of one kernel are the maps in turn, `reps` each).
+    Prints one JSON line of per-map median microseconds and GB/s."""
+    import numpy as np
+    import torch
+
+    import load_balancing_amd as mx
+    import synth
+
+    dev = torch.device("cuda:0")
+    base = synth.WORKLOADS["sweep"]
+    R, E, S, K, H = base.R, base.E, base.S, base.K, base.H
+    N, NK = R * S, R * S * K
+    s = mx.Shape(R, E, S, K, H)
+    b = mx.allocate(s, dev)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    rng = np.random.default_rng(seed)
+    maps = {"identity": up(np.arange(NK, dtype=np.int32))}
+    for name, lv in (("plan mv0", 0.0), ("plan mv4", 4.0)):
+        tk, _ = synth.routing(synth.sweep_workload(lv, seed), seed)
+        mx.plan_step(b, up(tk))
+        maps[name] = b.slot_of.clone()
+    # a uniform random expert per entry, NK/E entries each, each expert's rows
+    # contiguous and in entry order: a stable sort of shuffled expert labels
+    keys = rng.permutation(np.repeat(np.arange(E, dtype=np.int64), NK // E))
+    order = np.argsort(keys, kind="stable")
+    uni = np.empty(NK, dtype=np.int32)
+    uni[order] = np.arange(NK, dtype=np.int32)
+    maps["uniform expert"] = up(uni)
+    maps["random permutation"] = up(rng.permutation(NK).astype(np.int32))
+    _, gates = synth.routing(synth.sweep_workload(4.0, seed), seed)
+    g = up(gates)
+    x = up(synth.activations(base, seed).view(np.int16)).view(torch.bfloat16)
+    dy = up(synth.activations(base, seed, synth.TAG_DY).view(np.int16)).view(torch.bfloat16)
+    y = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    d_out = torch.empty((NK, H), dtype=torch.bfloat16, device=dev)
+    d_g = torch.empty(NK, dtype=torch.float32, device=dev)
+    dx = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
+    flush_buf = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    calls = {
+        "dispatch": lambda so: mx.moonep_dispatch(s, x, so, b.buf, stream),
+        "combine": lambda so: mx.moonep_combine(s, b.buf, g, so, y, stream),
+        "combine_bwd": lambda so: mx.moonep_combine_bwd(s, dy, b.buf, g, so, d_out, d_g, stream),
+        "dispatch_bwd": lambda so: mx.moonep_dispatch_bwd(s, d_out, so, dx, stream),
+    }
+    byt = algorithmic_bytes(R, S, K, H)
+    ev = {}
+    for name in MAP_STUDY:
+        for call, fn in calls.items():
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                flush_buf.sum()
+                e0.record(stream)
+                fn(maps[name])
+                e1.record(stream)
+                ev.setdefault((name, call), []).append((e0, e1))
+    torch.cuda.synchronize()
+    out = {}
+    for (name, call), pairs in ev.items():
+        t = sorted(e0.elapsed_time(e1) for e0, e1 in pairs)[len(pairs) // 2]
+        out.setdefault(name, {})[call] = {"us": round(1e3 * t, 1),
+                                          "GBps": round(byt[call] / (1e-3 * t) / 1e9, 1)}
+    print(json.dumps({"map_study": out, "reps": reps, "workload": WORKLOAD_NAME["sweep"],
+                      "cache": "untimed 512 MiB read before each call"}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,7 +474,13 @@ def main():
                     help="skip the untimed 1 GiB copy used to calibrate HBM counters")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the untimed 512 MiB cache-evicting read before each mover")
+    ap.add_argument("--map-study", action="store_true",
+                    help="diagnostic: time the movers over non-plan destination maps (identity, "
+                         "uniform expert, random permutation) beside two plans, then exit")
     args = ap.parse_args()
+    if args.map_study:
+        map_study()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark measures one GPU: R logical ranks are slices of one "
                                    "device's HBM, so --gpus must be 1"}))
