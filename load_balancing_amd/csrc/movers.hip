@@ -50,10 +50,11 @@ inline int block_for(int32_t V)
 // Resident waves per CU that measured best on gfx950 for each mover in the
 // full step on the expert-grouped access pattern, each call starting with
 // the MALL and L2 evicted (HBM efficiency falls when more scattered row
-// requests are in flight; too few leave it idle): dispatch 12, combine 12,
-// combine_bwd 16, dispatch_bwd 12 -- 3, 3, 4 and 3 workgroups of 256 threads.
+// requests are in flight; too few leave it idle): dispatch 12, combine 16,
+// combine_bwd 16, dispatch_bwd 12 -- 3, 4, 4 and 3 workgroups of 256 threads.
 // On the 1.2 GB sweep step: dispatch 225 us at 12 against 231-235 at 8, 16
-// and 20; combine 198 us at 12 against 210 at 8 and 209 at 16; combine_bwd
+// and 20; combine (fp64 sums, 118 VGPRs) 198-203 us at 16 against 205-207 at
+// 12 and 225 at 8 (with the earlier fp32 chain, 198 at 12 and 209 at 16); combine_bwd
 // 431 us at 16 against 445 at 12; dispatch_bwd, whose fp64 sums need 154
 // VGPRs, 228 us at 8 and 203 at 12-20.  Dispatch of rows longer than one
 // 256-thread workgroup (H = 4096 and 7168) runs one 64-thread workgroup per
@@ -65,8 +66,9 @@ inline int block_for(int32_t V)
 // combine_bwd of rows longer than one workgroup (each thread looping over
 // several vectors) does better at 12: 3252-3294 us against 3388 at 16 on the
 // adversarial shape (H = 4096), no change on the DeepSeek-V3-like one.
-constexpr int kDispatchWaves = 12, kDispatchBlocksWaves = 24, kCombineWaves = 12,
-              kCombineBwdWaves = 16, kCombineBwdLongWaves = 12, kDispatchBwdWaves = 12;
+constexpr int kDispatchWaves = 12, kDispatchBlocksWaves = 24, kCombineWaves = 16,
+              kCombineBlocksWaves = 12, kCombineBwdWaves = 16, kCombineBwdLongWaves = 12,
+              kDispatchBwdWaves = 12;
 
 // Dynamic LDS a workgroup of `threads` requests so that only
 // waves_per_cu / (threads / 64) of them fit in one CU's LDS; the kernels do not
@@ -435,7 +437,8 @@ void run_combine(dim3 g, dim3 b, hipStream_t st, const u32x4 *out, const float *
                  const int32_t *so, u32x4 *y, int64_t N, int32_t V, int32_t nwb, int32_t cpb,
                  int32_t K, uint32_t nrows)
 {
-    hipLaunchKernelGGL(combine_kernel<KT>, g, b, residency_lds(kCombineWaves, (int)b.x), st, out,
+    const int waves = b.x == kBlock ? kCombineWaves : kCombineBlocksWaves;
+    hipLaunchKernelGGL(combine_kernel<KT>, g, b, residency_lds(waves, (int)b.x), st, out,
                        gates, so, y, N, V, nwb, cpb, K, nrows);
 }
 
