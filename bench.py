@@ -235,7 +235,7 @@ def cpu_baseline_sampled(w, seed, ntok=2048):
                       f"bytes / time"}
 
 
-def plan_latency(mx, s, b, topks, levels, stream, reps=20):
+def plan_latency(mx, s, b, topks, levels, stream, reps=20, planner=None):
     """Median HIP-event time of route_stats + plan per routing level, over
     `reps` pairs on the launching stream (after the timed steps).  Each pair
     sits behind a ~40 us device copy, so the host has queued both launches
@@ -247,10 +247,11 @@ def plan_latency(mx, s, b, topks, levels, stream, reps=20):
     ahead_dst = torch.empty_like(ahead_src)
     out = {}
     for lv, tk in zip(levels, topks):
+        plan_fn = planner or mx.moonep_plan
+
         def pair():
             mx.moonep_route_stats(s, tk, b.expert_counts, b.maxvio, b.workspace, stream)
-            mx.moonep_plan(s, tk, b.expert_counts, b.workspace, b.plan, b.slot_of, b.src_of_slot,
-                           stream)
+            plan_fn(s, tk, b.expert_counts, b.workspace, b.plan, b.slot_of, b.src_of_slot, stream)
         for _ in range(3):
             pair()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -266,7 +267,7 @@ def plan_latency(mx, s, b, topks, levels, stream, reps=20):
     return out
 
 
-def seed_leg(mx, s, b, y, seed, flush, stream, reps=4):
+def seed_leg(mx, s, b, y, seed, flush, stream, reps=4, planner=None):
     """The sweep levels of another seed (its own bisected Zipf exponents,
     tokens and gates), timed as in the steps: dispatch+combine GB/s over
     `reps` evicted-cache passes per level, and route_stats + plan per level
@@ -287,8 +288,8 @@ def seed_leg(mx, s, b, y, seed, flush, stream, reps=4):
     n_rep, maxvio, ev = {}, {}, []
     for lv, tk, gt in zip(levels, topks, gts):
         mx.moonep_route_stats(s, tk, b.expert_counts, b.maxvio, b.workspace, stream)
-        mx.moonep_plan(s, tk, b.expert_counts, b.workspace, b.plan, b.slot_of, b.src_of_slot,
-                       stream)
+        (planner or mx.moonep_plan)(s, tk, b.expert_counts, b.workspace, b.plan, b.slot_of,
+                                    b.src_of_slot, stream)
         n_rep[lv] = int(b.plan_fields()["n_rep"])
         maxvio[lv] = round(float(b.maxvio.item()), 4)
         for _ in range(reps):
@@ -307,7 +308,7 @@ def seed_leg(mx, s, b, y, seed, flush, stream, reps=4):
     ms = sum(e[0].elapsed_time(e[1]) + e[2].elapsed_time(e[3]) for e in ev)
     byt = algorithmic_bytes(s.R, s.S, s.K, s.H)
     gbps = len(ev) * (byt["dispatch"] + byt["combine"]) / (1e-3 * ms) / 1e9
-    plan_us = plan_latency(mx, s, b, topks, levels, stream)
+    plan_us = plan_latency(mx, s, b, topks, levels, stream, planner=planner)
     pv = list(plan_us.values())
     return {"value": round(gbps, 1), "frac_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
             "plan_us_vs_maxvio": plan_us, "plan_spread": round((max(pv) - min(pv)) / min(pv), 4),
@@ -474,6 +475,9 @@ def main():
                     help="skip the untimed 1 GiB copy used to calibrate HBM counters")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the untimed 512 MiB cache-evicting read before each mover")
+    ap.add_argument("--planner", default="lowest-id", choices=("lowest-id", "largest-first"),
+                    help="moonep_plan (overfull ranks spill from their lowest expert id) or "
+                         "moonep_plan_largest_first (from their largest count: fewer replicas)")
     ap.add_argument("--map-study", action="store_true",
                     help="diagnostic: time the movers over non-plan destination maps (identity, "
                          "uniform expert, random permutation) beside two plans, then exit")
@@ -550,6 +554,7 @@ def main():
     dx = torch.empty((N, H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
     flush_buf = torch.ones(1 << 27, dtype=torch.float32, device=dev)   # 512 MiB
+    planner = mx.moonep_plan_largest_first if args.planner == "largest-first" else mx.moonep_plan
 
     def flush():
         if not args.no_flush:
@@ -560,7 +565,7 @@ def main():
         tk, gt = topks[lv], gatess[lv]
         calls = (
             lambda: mx.moonep_route_stats(s, tk, b.expert_counts, b.maxvio, b.workspace, stream),
-            lambda: mx.moonep_plan(s, tk, b.expert_counts, b.workspace, b.plan, b.slot_of,
+            lambda: planner(s, tk, b.expert_counts, b.workspace, b.plan, b.slot_of,
                                    b.src_of_slot, stream),
             lambda: mx.moonep_weight_slots(s, b.plan, B_slots, wslot, stream),
             lambda: mx.moonep_prefetch_weights(s, b.plan, wslot, B_slots, wbytes, w_home, pool,
@@ -646,7 +651,7 @@ def main():
                         0.5 * (sorted(v)[len(v) // 2 - 1] + sorted(v)[len(v) // 2]))
     plan_us_in_step = {lv: round(1e3 * median(v), 2) for lv, v in plan_in_step.items() if v}
     pis = list(plan_us_in_step.values())
-    plan_us = plan_latency(mx, s, b, topks, levels, stream)
+    plan_us = plan_latency(mx, s, b, topks, levels, stream, planner=planner)
     pv = list(plan_us.values())
     kern = {}
     for name in MOVERS + ("replica_grad_reduce", "prefetch"):
@@ -690,7 +695,7 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAME[args.workload],
-                   "R": R, "E": E, "S": S, "K": K, "H": H, "G": G,
+                   "R": R, "E": E, "S": S, "K": K, "H": H, "G": G, "planner": args.planner,
                    "global_batch": N, "parallelism": f"1 GPU, {R} logical ranks"},
         "frac_hbm_peak": round(value / HBM_PEAK_GBPS, 4),
         "value_def": "dispatch+combine algorithmic bytes / their HIP-event time",
@@ -723,7 +728,7 @@ def main():
     }
     if args.workload == "sweep" and args.extra_seeds:
         result["other_seeds"] = {
-            sd: seed_leg(mx, s, b, y, int(sd), flush, stream)
+            sd: seed_leg(mx, s, b, y, int(sd), flush, stream, planner=planner)
             for sd in args.extra_seeds.split(",") if int(sd) != args.seed}
     if args.workload == "tiny":
         result["expert_gemm"] = {"skipped": "H = 64 is below the grouped GEMM's 128-column "

@@ -86,8 +86,8 @@ int moonep_check_shape(const moonep_shape *shape);
  * and the device error word.  Zero it once when it is allocated; the calls
  * keep it consistent afterwards.  One workspace serves one route_stats ->
  * plan sequence at a time: sequences that may overlap (on different streams)
- * need workspaces of their own, since they would share its counts and the
- * completion counter route_stats keeps there.  Returns 0 for an invalid shape.
+ * need workspaces of their own, since they would share its counts.  Returns 0
+ * for an invalid shape.
  */
 size_t moonep_workspace_bytes(const moonep_shape *shape);
 

@@ -28,8 +28,8 @@ constexpr int kMinSegments = 1024, kMaxSegments = 2048, kSegmentEntries = 512;
 constexpr int kChunkBatch = 16;        // 64-entry chunks loaded ahead per wave
 constexpr size_t kCtlBytes = 256;      // workspace control block
 
-// Workspace control block (int32 words).
-enum { kCtlError = 0, kCtlTicket = 1 };
+// Workspace control block (int32 words): the sticky device error word.
+enum { kCtlError = 0 };
 
 struct WsLayout {
     int64_t nk;      // routed entries R*S*K

@@ -12,8 +12,9 @@
 //            skewed the routing is) and stores it column-wise, [E][nseg].
 //   rs_scan: one workgroup per expert turns its column into exclusive
 //            per-segment bases (the stable start of each segment within the
-//            expert, used by the slot assignment) and the total T_e.  The last
-//            workgroup to finish computes Tmax and maxvio.
+//            expert, used by the slot assignment) and the total T_e.  maxvio
+//            is an atomic max over the experts (see rs_scan_kernel), so no
+//            workgroup waits for the others.
 #include "moonep_internal.hpp"
 
 namespace moonep {
@@ -21,7 +22,8 @@ namespace moonep {
 __global__ __launch_bounds__(kBlock) void rs_hist_kernel(const int32_t *__restrict__ topk, int64_t nk,
                                                          int32_t E, int32_t segw, int32_t nseg,
                                                          int32_t nbits, int32_t *__restrict__ hist,
-                                                         int32_t *__restrict__ ctl)
+                                                         int32_t *__restrict__ ctl,
+                                                         float *__restrict__ maxvio)
 {
     extern __shared__ int32_t lds[];
     const int wid = (int)threadIdx.x >> 6;
@@ -30,7 +32,7 @@ __global__ __launch_bounds__(kBlock) void rs_hist_kernel(const int32_t *__restri
     for (int e = lane; e < E; e += 64)
         h[e] = 0;
     if (blockIdx.x == 0 && threadIdx.x == 0)
-        ctl[kCtlTicket] = 0;  // rs_scan runs after this launch completes
+        maxvio[0] = 0.0f;  // the start of rs_scan's atomic max, which runs after this launch
     __syncthreads();
 
     const int32_t seg = (int32_t)blockIdx.x * kWaves + wid;
@@ -69,15 +71,17 @@ __global__ __launch_bounds__(kBlock) void rs_hist_kernel(const int32_t *__restri
         hist[(int64_t)e * nseg + seg] = h[e];
 }
 
+// maxvio = fp32((Tmax*E)/nk - 1) is the largest of the experts' fp32((T_e*E)/nk
+// - 1): division by nk, the subtraction and the rounding are all monotonic.
+// That largest value is >= +0 (Tmax is at least the mean), so an integer max
+// of the fp32 bit patterns, started at +0 by rs_hist, finds it: a negative
+// value's pattern is a negative integer and never wins.
 __global__ __launch_bounds__(kBlock) void rs_scan_kernel(int32_t *__restrict__ hist, int32_t nseg,
                                                          int32_t E, int64_t nk,
                                                          int32_t *__restrict__ counts,
-                                                         float *__restrict__ maxvio,
-                                                         int32_t *__restrict__ ctl)
+                                                         float *__restrict__ maxvio)
 {
     __shared__ int tmp[kWaves];
-    __shared__ int is_last;
-    __shared__ int red[kWaves];
     const int e = (int)blockIdx.x;
     int32_t *col = hist + (int64_t)e * nseg;
     constexpr int kPer = kMaxSegments / kBlock;    // entries per thread, at most
@@ -134,37 +138,13 @@ __global__ __launch_bounds__(kBlock) void rs_scan_kernel(int32_t *__restrict__ h
     }
     if (threadIdx.x == 0) {
         counts[e] = total;
-        __threadfence();
-        const int ticket = atomicAdd(&ctl[kCtlTicket], 1);
-        is_last = ticket == E - 1;
-    }
-    __syncthreads();
-    if (!is_last)
-        return;
-    __threadfence();
-    int m = 0;
-    for (int i = (int)threadIdx.x; i < E; i += kBlock) {
-        const int c = __hip_atomic_load(&counts[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        m = c > m ? c : m;
-    }
-    for (int d = 32; d > 0; d >>= 1) {
-        const int o = __shfl_xor(m, d, 64);
-        m = o > m ? o : m;
-    }
-    if (lane_id() == 0)
-        red[threadIdx.x >> 6] = m;
-    __syncthreads();
-    if (threadIdx.x == 0) {
-        int tmax = 0;
-        for (int w = 0; w < kWaves; ++w)
-            tmax = red[w] > tmax ? red[w] : tmax;
         if (nk == 0) {
-            maxvio[0] = 0.0f;
+            if (e == 0)
+                maxvio[0] = 0.0f;  // rs_hist does not run without entries
         } else {
-            const double ratio = (double)((int64_t)tmax * E) / (double)nk;
-            maxvio[0] = (float)(ratio - 1.0);
+            const double ratio = (double)((int64_t)total * E) / (double)nk;
+            atomicMax((int *)maxvio, __float_as_int((float)(ratio - 1.0)));
         }
-        ctl[kCtlTicket] = 0;  // ready for the next call even if rs_hist is skipped
     }
 }
 
@@ -178,10 +158,10 @@ int launch_route_stats(const moonep_shape &s, const int32_t *topk, int32_t *coun
         const int blocks = (w.nseg + kWaves - 1) / kWaves;
         const size_t lds = (size_t)kWaves * s.E * sizeof(int32_t);
         hipLaunchKernelGGL(rs_hist_kernel, dim3(blocks), dim3(kBlock), lds, st, topk, w.nk, s.E,
-                           w.segw, w.nseg, expert_bits(s.E), hist, ctl);
+                           w.segw, w.nseg, expert_bits(s.E), hist, ctl, maxvio);
     }
     hipLaunchKernelGGL(rs_scan_kernel, dim3(s.E), dim3(kBlock), 0, st, hist, w.nseg, s.E, w.nk,
-                       counts, maxvio, ctl);
+                       counts, maxvio);
     return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
 }
 
