@@ -478,11 +478,16 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
             }
             const uint64_t same = match_lanes(e, active, nbits);
             const int ee = ok ? e : 0;
-            const int32_t pos = run[ee] + count_below(same);
-            wave_sync();
-            if (ok && (same >> lane) == 1ull)
-                run[ee] = pos + 1;  // the highest lane of a group holds its last position
-            wave_sync();
+            // The highest lane of each group of equal keys claims the group's
+            // positions with one LDS atomic add, which returns the expert's
+            // running count; the other lanes of the group read it from that
+            // lane.  LDS executes one wave's atomics in issue order, so the
+            // chunks need no barrier between them.
+            const int leader = 63 - __builtin_clzll(same | 1ull);
+            int32_t got = 0;
+            if (ok && leader == lane)
+                got = atomicAdd(&run[ee], __popcll(same));
+            const int32_t pos = __shfl(got, leader, 64) + count_below(same);
             // home destination and replica destination, both computed
             const int32_t kp = S.keep[ee];
             const int32_t home = S.home_dst[ee] + pos;

@@ -8,8 +8,8 @@
 //   rs_hist: one wave per contiguous segment of routed entries counts its
 //            experts into a private LDS histogram (one ballot per key bit
 //            finds the lanes sharing an expert, so the last lane of each
-//            group adds the group size: no atomics, time independent of how
-//            skewed the routing is) and stores it column-wise, [E][nseg].
+//            group adds the group size with one LDS atomic: time independent
+//            of how skewed the routing is) and stores it column-wise, [E][nseg].
 //   rs_scan: one workgroup per expert turns its column into exclusive
 //            per-segment bases (the stable start of each segment within the
 //            expert, used by the slot assignment) and the total T_e.  maxvio
@@ -60,8 +60,7 @@ __global__ __launch_bounds__(kBlock) void rs_hist_kernel(const int32_t *__restri
                 continue;
             const uint64_t same = match_lanes(e, active, nbits);
             if (ok && (same >> lane) == 1ull)  // highest lane of its group
-                h[e] += __popcll(same);
-            wave_sync();
+                atomicAdd(&h[e], __popcll(same));  // LDS; no barrier between chunks
         }
     }
     if (ballot(bad) != 0 && lane == 0)
