@@ -40,23 +40,25 @@ namespace {
 // LDS tables of the plan (int32).  E1 = E + 1, R1 = R + 1, CAP = E + R words.
 struct PlanLds {
     // per expert
-    int32_t *T, *P, *spill, *Sp, *sflag, *sidx, *keep, *home_dst, *rep_first, *rep_cnt;
+    int32_t *T, *P, *spill, *Sp, *keep, *home_dst, *rep_first, *rep_cnt;
     // spill list (A), index i < nA
     int32_t *Aval, *Aexp, *Aexcl, *posA;
     // per rank / deficit list (B), index j < nB
-    int32_t *load, *D, *dflag, *Dp, *didx, *Bval, *Brank, *Bexcl, *Bca, *nc, *NC, *posB;
+    int32_t *load, *Bval, *Brank, *Bexcl, *NC, *posB;
     // per replica (plan order)
     int32_t *U, *rai, *rbj, *rexp, *rhost, *rcnt, *rso, *rrow, *rdst;
     int32_t *misc;  // [16]: scalars of the plan header
     int32_t *run;   // [kWaves][E]: per-wave running counts
+    int32_t *keys0; // [kChunkBatch * 64]: wave 0's first keys, staged by wave 1
 };
 
-constexpr int kEArrays = 14, kRArrays = 12, kCArrays = 9;
+constexpr int kEArrays = 12, kRArrays = 6, kCArrays = 9;
 
 __host__ __device__ inline size_t plan_lds_words(int32_t E, int32_t R)
 {
     const size_t e1 = (size_t)E + 1, r1 = (size_t)R + 1, cap = (size_t)E + R;
-    return kEArrays * e1 + kRArrays * r1 + kCArrays * cap + 16 + (size_t)kWaves * E;
+    return kEArrays * e1 + kRArrays * r1 + kCArrays * cap + 16 + (size_t)kWaves * E +
+           (size_t)kChunkBatch * 64;
 }
 
 __device__ inline PlanLds carve(int32_t *base, int32_t E, int32_t R)
@@ -64,15 +66,14 @@ __device__ inline PlanLds carve(int32_t *base, int32_t E, int32_t R)
     PlanLds L;
     const int32_t e1 = E + 1, r1 = R + 1, cap = E + R;
     int32_t *p = base;
-    int32_t **e_arrays[kEArrays] = {&L.T, &L.P, &L.spill, &L.Sp, &L.sflag, &L.sidx, &L.keep,
-                                    &L.home_dst, &L.rep_first, &L.rep_cnt, &L.Aval, &L.Aexp,
-                                    &L.Aexcl, &L.posA};
+    int32_t **e_arrays[kEArrays] = {&L.T,         &L.P,         &L.spill,   &L.Sp,
+                                    &L.keep,      &L.home_dst,  &L.rep_first, &L.rep_cnt,
+                                    &L.Aval,      &L.Aexp,      &L.Aexcl,   &L.posA};
     for (int32_t **a : e_arrays) {
         *a = p;
         p += e1;
     }
-    int32_t **r_arrays[kRArrays] = {&L.load, &L.D, &L.dflag, &L.Dp, &L.didx, &L.Bval,
-                                    &L.Brank, &L.Bexcl, &L.Bca, &L.nc, &L.NC, &L.posB};
+    int32_t **r_arrays[kRArrays] = {&L.load, &L.Bval, &L.Brank, &L.Bexcl, &L.NC, &L.posB};
     for (int32_t **a : r_arrays) {
         *a = p;
         p += r1;
@@ -86,136 +87,93 @@ __device__ inline PlanLds carve(int32_t *base, int32_t E, int32_t R)
     L.misc = p;
     p += 16;
     L.run = p;
+    p += (size_t)kWaves * E;
+    L.keys0 = p;
     return L;
 }
 
-// Exclusive scan across the 64 lanes of a wave; *total = sum of all lanes.
-__device__ inline int wave_excl_scan(int v, int *total)
-{
-    const int lane = lane_id();
-    int incl = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d, 64);
-        if (lane >= d)
-            incl += o;
-    }
-    *total = __shfl(incl, 63, 64);
-    return incl - v;
-}
+// Cross-lane steps on DPP (data-parallel primitives of the VALU): each is one
+// vector instruction with no LDS round trip.  row_shr:n reads lane i - n of
+// the same 16-lane row (zero when that lane is outside the row);
+// row_bcast:15 and row_bcast:31 (gfx9) hand the last lane of row r - 1, or
+// lane 31, to the rows the row mask enables.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118,
+              kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
 
-__device__ inline int wave_max(int v)
+// Inclusive sum over lanes 0..l of v, in lane l (every lane of the wave active).
+__device__ __forceinline__ int32_t wave_incl_sum(int32_t v)
 {
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-        const int o = __shfl_xor(v, d, 64);
-        v = o > v ? o : v;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xa, 0xf, false);  // rows 1 and 3
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xc, 0xf, false);  // rows 2 and 3
     return v;
 }
 
-// One wave: exclusive scan of in[0..n) into out[0..n], out[n] = total.  Lane
-// l owns the contiguous run [l*per, (l+1)*per).  Returns the total.
-__device__ int wave_scan_array(const int32_t *in, int32_t *out, int n)
+// Largest v over the wave, for v >= 0 (every lane active).
+__device__ __forceinline__ int32_t wave_max_nonneg(int32_t v)
 {
-    const int lane = lane_id();
-    const int per = (n + 63) / 64;
-    const int first = lane * per;
-    int sum = 0;
-    for (int i = 0; i < per; ++i)
-        if (first + i < n)
-            sum += in[first + i];
-    int total = 0;
-    int run = wave_excl_scan(sum, &total);
-    for (int i = 0; i < per; ++i)
-        if (first + i < n) {
-            const int v = in[first + i];
-            out[first + i] = run;
-            run += v;
-        }
-    if (lane == 0)
-        out[n] = total;
-    wave_sync();
-    return total;
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xa, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xc, 0xf, false));
+    return __builtin_amdgcn_readlane(v, 63);
 }
 
-// Four independent exclusive scans in one pass, so that their shuffle chains
-// interleave: in0/in1 over n01 entries, in2/in3 over n23 entries, each laid
-// out as in wave_scan_array (out[n] = total).  Returns the totals of in1 and
-// in3 (the list lengths when those are 0/1 flags).
-__device__ void wave_scan_arrays4(const int32_t *in0, int32_t *out0, const int32_t *in1,
-                                  int32_t *out1, int n01, const int32_t *in2, int32_t *out2,
-                                  const int32_t *in3, int32_t *out3, int n23, int *tot1, int *tot3)
+// Exclusive scans of A arrays held in registers: value i of lane l sits at
+// position l + 64 i of its array.  ex[a][i] = sum of array a's values at
+// earlier positions; tot[a] = the sum of all of them.  The A x N chains are
+// independent of one another, so they interleave.
+template <int A, int N>
+__device__ inline void strided_scan(const int32_t (&v)[A][N], int32_t (&ex)[A][N], int32_t (&tot)[A])
 {
-    const int lane = lane_id();
-    const int pa = (n01 + 63) / 64, pb = (n23 + 63) / 64;
-    const int fa = lane * pa, fb = lane * pb;
-    int s0 = 0, s1 = 0, s2 = 0, s3 = 0;
-    for (int i = 0; i < pa; ++i)
-        if (fa + i < n01) {
-            s0 += in0[fa + i];
-            s1 += in1[fa + i];
-        }
-    for (int i = 0; i < pb; ++i)
-        if (fb + i < n23) {
-            s2 += in2[fb + i];
-            s3 += in3[fb + i];
-        }
-    int c0 = s0, c1 = s1, c2 = s2, c3 = s3;
+    int32_t inc[A][N];
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o0 = __shfl_up(c0, d, 64), o1 = __shfl_up(c1, d, 64);
-        const int o2 = __shfl_up(c2, d, 64), o3 = __shfl_up(c3, d, 64);
-        if (lane >= d) {
-            c0 += o0;
-            c1 += o1;
-            c2 += o2;
-            c3 += o3;
+    for (int a = 0; a < A; ++a)
+#pragma unroll
+        for (int i = 0; i < N; ++i)
+            inc[a][i] = wave_incl_sum(v[a][i]);
+#pragma unroll
+    for (int a = 0; a < A; ++a) {
+        int32_t base = 0;
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            ex[a][i] = base + inc[a][i] - v[a][i];
+            base += __builtin_amdgcn_readlane(inc[a][i], 63);
         }
+        tot[a] = base;
     }
-    const int t0 = __shfl(c0, 63, 64), t1 = __shfl(c1, 63, 64);
-    const int t2 = __shfl(c2, 63, 64), t3 = __shfl(c3, 63, 64);
-    int r0 = c0 - s0, r1 = c1 - s1, r2 = c2 - s2, r3 = c3 - s3;
-    for (int i = 0; i < pa; ++i)
-        if (fa + i < n01) {
-            const int v0 = in0[fa + i], v1 = in1[fa + i];
-            out0[fa + i] = r0;
-            out1[fa + i] = r1;
-            r0 += v0;
-            r1 += v1;
-        }
-    for (int i = 0; i < pb; ++i)
-        if (fb + i < n23) {
-            const int v2 = in2[fb + i], v3 = in3[fb + i];
-            out2[fb + i] = r2;
-            out3[fb + i] = r3;
-            r2 += v2;
-            r3 += v3;
-        }
-    if (lane == 0) {
-        out0[n01] = t0;
-        out1[n01] = t1;
-        out2[n23] = t2;
-        out3[n23] = t3;
-    }
-    wave_sync();
-    *tot1 = t1;
-    *tot3 = t3;
 }
 
-// Number of values of the strictly increasing a[0..n) below x, with a fixed
-// number of steps (2^steps > every n this is called with), so that the time
-// does not depend on n.
-__device__ inline int count_below_sorted(const int32_t *a, int n, int32_t x, int steps)
+// For each x1[i]: the number of values of the strictly increasing
+// s1[0..n1) below it, and likewise for x2 in s2, in a fixed number of steps
+// (2^steps > n1 and n2) so that the time does not depend on n1 and n2.  All
+// the searches advance together, one LDS read each per step.
+template <int N>
+__device__ inline void count_below_sorted2(const int32_t *s1, int n1, const int32_t (&x1)[N],
+                                           int32_t (&c1)[N], const int32_t *s2, int n2,
+                                           const int32_t (&x2)[N], int32_t (&c2)[N], int steps)
 {
-    int c = 0;  // a[0..c) < x
-    for (int st = steps; st >= 0; --st) {
-        const int t = c + (1 << st);
-        const bool in = t <= n;
-        const bool below = in && a[(in ? t : 1) - 1] < x;
-        c = below ? t : c;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+        c1[i] = 0;
+        c2[i] = 0;
     }
-    return c;
+    for (int st = steps; st >= 0; --st) {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+            const int t1 = c1[i] + (1 << st), t2 = c2[i] + (1 << st);
+            const bool in1 = t1 <= n1, in2 = t2 <= n2;
+            const int32_t v1 = s1[(in1 ? t1 : 1) - 1];
+            const int32_t v2 = s2[(in2 ? t2 : 1) - 1];
+            c1[i] = (in1 & (v1 < x1[i])) ? t1 : c1[i];  // '&': the reads stay unconditional
+            c2[i] = (in2 & (v2 < x2[i])) ? t2 : c2[i];
+        }
+    }
 }
 
 __host__ __device__ inline int ceil_log2(int v)
@@ -229,154 +187,313 @@ __host__ __device__ inline int ceil_log2(int v)
 // The whole plan, computed by one wave into the LDS tables.  policy 0: an
 // overfull rank spills from its lowest expert id; policy 1: from its largest
 // count, ties to the lower id.
-__device__ void wave_plan(const PlanLds &S, const int32_t *__restrict__ counts, int32_t R,
-                          int32_t E, int32_t C, int32_t policy)
+//
+// Lane l owns experts l, l + 64, ..., and ranks (and list entries) l, l + 64,
+// ...: PE of each, PE >= E / 64 >= R / 64.  Each step first reads what it
+// needs for all of the lane's items, then computes, then stores, so a
+// step's LDS reads are in flight together instead of one round trip per
+// item; the scans run on registers.  Everything does the same work whatever
+// the data: reads use clamped indices, and a lane with nothing to store
+// writes a spare slot that no plan uses (index E of an expert array: at
+// least one rank is not overfull, so at most E - 1 experts spill; index R of
+// a rank array: when C > 0 at least one rank is not underfull; index cap - 1
+// of a replica array: n_rep <= nA + nB - 1 <= cap - 2).  So the plan takes
+// the same time with or without replicas.
+template <int PE>
+__device__ void wave_plan(const PlanLds &S, int32_t (&t)[PE], int32_t R, int32_t E, int32_t C,
+                          int32_t policy)
 {
     const int lane = lane_id();
     const int32_t Lx = E / R;
     const int32_t cap = E + R;
 
-    // rank loads before balancing
-    for (int e = lane; e < E; e += 64)
-        S.T[e] = counts[e];
-    wave_sync();
-    wave_scan_array(S.T, S.P, E);
-    for (int r = lane; r < R; r += 64) {
-        const int32_t ld = S.P[(r + 1) * Lx] - S.P[r * Lx];
-        S.load[r] = ld;
-        S.D[r] = ld < C ? C - ld : 0;
-        S.dflag[r] = ld < C ? 1 : 0;
+    // ---- expert counts (t[i]: expert lane + 64 i) and their prefix P -------
+    int tmax = 0;
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+        t[i] = lane + 64 * i < E ? t[i] : 0;
+        tmax = t[i] > tmax ? t[i] : tmax;
     }
+    int32_t p[1][PE], ptot[1];
+    {
+        int32_t tt[1][PE];
+#pragma unroll
+        for (int i = 0; i < PE; ++i)
+            tt[0][i] = t[i];
+        strided_scan<1, PE>(tt, p, ptot);
+    }
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E) {
+            S.T[e] = t[i];
+            S.P[e] = p[0][i];
+        }
+    }
+    if (lane == 0)
+        S.P[E] = ptot[0];
     wave_sync();
-    // Everything below does the same work whatever the data: loads use
-    // clamped indices, and a lane with nothing to store writes a spare slot
-    // that no plan uses (index E of an expert array: at least one rank is not
-    // overfull, so at most E - 1 experts spill; index R of a rank array: when
-    // C > 0 at least one rank is not underfull; index cap - 1 of a replica
-    // array: n_rep <= nA + nB - 1 <= cap - 2).  So the plan takes the same
-    // time with or without replicas.
 
-    // whole-expert spill of overfull ranks: what the experts taken before e
-    // hold is the prefix of the rank's counts (lowest id first), or the sum of
-    // the rank's counts ordered before e by (count descending, id ascending)
-    // -- L steps for every expert, whatever the counts
-    for (int e = lane; e < E; e += 64) {
-        const int32_t r = e / Lx;
-        const int32_t excess = S.load[r] - C;
-        int32_t before = S.P[e] - S.P[r * Lx];
+    // ---- rank loads, deficits, and the whole-expert spill -----------------
+    // P at the first expert of each owned rank and of each owned expert's rank
+    int32_t ra[PE], rb[PE], prs[PE], pre[PE];
+#pragma unroll
+    for (int j = 0; j < PE; ++j) {
+        const int r = lane + 64 * j;
+        const int rc = r < R ? r : R - 1;
+        ra[j] = S.P[rc * Lx];
+        rb[j] = S.P[(rc + 1) * Lx];
+    }
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+        const int e = lane + 64 * i;
+        const int r = (e < E ? e : E - 1) / Lx;
+        prs[i] = S.P[r * Lx];
+        pre[i] = S.P[(r + 1) * Lx];
+    }
+    int32_t sc[4][PE];  // spill, spill flag (per expert); deficit, deficit flag (per rank)
+#pragma unroll
+    for (int j = 0; j < PE; ++j) {
+        const int r = lane + 64 * j;
+        const int32_t ld = rb[j] - ra[j];
+        if (r < R)
+            S.load[r] = ld;
+        sc[2][j] = r < R && ld < C ? C - ld : 0;
+        sc[3][j] = r < R && ld < C ? 1 : 0;
+    }
+    // what the experts taken before e hold: the prefix of the rank's counts
+    // (lowest id first), or the sum of the rank's counts ordered before e by
+    // (count descending, id ascending)
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+        const int e = lane + 64 * i;
+        const int32_t excess = (pre[i] - prs[i]) - C;
+        int32_t before = p[0][i] - prs[i];
         if (policy == 1) {
-            const int32_t te = S.T[e];
+            const int32_t te = t[i];
+            const int32_t k1 = (e < E ? e : E - 1) / Lx * Lx, kend = k1 + Lx;
             before = 0;
-            for (int32_t k = r * Lx; k < (r + 1) * Lx; ++k) {
-                const int32_t tk = S.T[k];
-                before += tk > te || (tk == te && k < e) ? tk : 0;
+            for (int32_t k0 = k1; k0 < kend; k0 += 8) {
+                int32_t tk[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    tk[u] = S.T[k0 + u < kend ? k0 + u : kend - 1];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int32_t k = k0 + u;
+                    before += k < kend && (tk[u] > te || (tk[u] == te && k < e)) ? tk[u] : 0;
+                }
             }
         }
         int32_t give = excess - before;
-        give = give < 0 ? 0 : (give > S.T[e] ? S.T[e] : give);
-        give = excess > 0 ? give : 0;
-        S.spill[e] = give;
-        S.keep[e] = S.T[e] - give;
-        S.sflag[e] = give > 0 ? 1 : 0;
+        give = give < 0 ? 0 : (give > t[i] ? t[i] : give);
+        give = excess > 0 && e < E ? give : 0;
+        sc[0][i] = give;
+        sc[1][i] = give > 0 ? 1 : 0;
+        if (e < E) {
+            S.spill[e] = give;
+            S.keep[e] = t[i] - give;
+        }
     }
-    wave_sync();
-    int nA = 0, nB = 0;
-    wave_scan_arrays4(S.spill, S.Sp, S.sflag, S.sidx, E, S.D, S.Dp, S.dflag, S.didx, R, &nA, &nB);
-
-    // compact the spill (A) and deficit (B) lists
-    for (int e = lane; e < E; e += 64) {
-        const int32_t r = e / Lx;
-        const int i = S.spill[e] > 0 ? S.sidx[e] : E;
-        S.Aval[i] = S.Sp[e] + S.spill[e];
-        S.Aexp[i] = e;
-        S.Aexcl[i] = S.Sp[e];
-        // first destination row of expert e at home: rank base + earlier keeps
-        S.home_dst[e] = r * C + (S.P[e] - S.P[r * Lx]) - (S.Sp[e] - S.Sp[r * Lx]);
-        S.rep_first[e] = 0;
-        S.rep_cnt[e] = 0;
-    }
-    for (int r = lane; r < R; r += 64) {
-        const int j = S.D[r] > 0 ? S.didx[r] : R;
-        S.Bval[j] = S.Dp[r] + S.D[r];
-        S.Brank[j] = r;
-        S.Bexcl[j] = S.Dp[r];
+    int32_t sx[4][PE], stot[4];
+    strided_scan<4, PE>(sc, sx, stot);
+    const int nA = stot[1], nB = stot[3];
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+        const int e = lane + 64 * i;
+        if (e < E)
+            S.Sp[e] = sx[0][i];
     }
     wave_sync();
 
-    // The loops below run over all E (or R) slots with the list length as a
-    // predicate, and the searches have fixed depth.
-    const int ea = ceil_log2(E + 1), rb = ceil_log2(R + 1);
+    // ---- the spill (A) and deficit (B) lists, compacted; home rows -------
+    int32_t sprs[PE];
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+        const int e = lane + 64 * i;
+        sprs[i] = S.Sp[(e < E ? e : E - 1) / Lx * Lx];
+    }
+#pragma unroll
+    for (int i = 0; i < PE; ++i) {
+        const int e = lane + 64 * i;
+        const int a = e < E && sc[0][i] > 0 ? sx[1][i] : E;
+        S.Aval[a] = sx[0][i] + sc[0][i];
+        S.Aexp[a] = e;
+        S.Aexcl[a] = sx[0][i];
+        if (e < E) {
+            const int32_t r = e / Lx;
+            // first destination row of expert e at home: rank base + earlier keeps
+            S.home_dst[e] = r * C + (p[0][i] - prs[i]) - (sx[0][i] - sprs[i]);
+            S.rep_first[e] = 0;
+            S.rep_cnt[e] = 0;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < PE; ++j) {
+        const int r = lane + 64 * j;
+        const int b = r < R && sc[2][j] > 0 ? sx[3][j] : R;
+        S.Bval[b] = sx[2][j] + sc[2][j];
+        S.Brank[b] = r;
+        S.Bexcl[b] = sx[2][j];
+    }
+    wave_sync();
 
+    // ---- the union of both lists' running totals -------------------------
+    // Two searches of fixed depth, run side by side: each deficit total's
+    // place among the spill totals (bca) and each spill total's among the
+    // deficit totals (cb).  Both take the depth of the E-entry list; the
+    // extra steps of the shorter list's search change nothing (2^ea > E >= R).
+    const int ea = ceil_log2(E + 1);
+    int32_t bv[PE], bca[PE], avi[PE], cb[PE], ncv[1][PE];
+#pragma unroll
+    for (int k = 0; k < PE; ++k) {
+        const int kk = lane + 64 * k;
+        bv[k] = S.Bval[kk < R ? kk : R];
+        avi[k] = S.Aval[kk < E ? kk : E];
+    }
+    {
+        int32_t xb[PE], xa[PE];
+#pragma unroll
+        for (int k = 0; k < PE; ++k) {
+            xb[k] = lane + 64 * k < nB ? bv[k] : 0;
+            xa[k] = lane + 64 * k < nA ? avi[k] : 0;
+        }
+        count_below_sorted2<PE>(S.Aval, nA, xb, bca, S.Bval, nB, xa, cb, ea);
+    }
     // deficit totals that coincide with a spill total
-    for (int j = lane; j < R; j += 64) {
-        const bool live = j < nB;
-        const int a = count_below_sorted(S.Aval, nA, live ? S.Bval[j] : 0, ea);
-        S.Bca[j] = a;
-        S.nc[j] = live && !(a < nA && S.Aval[a] == S.Bval[j]) ? 1 : 0;  // 1 = not shared with A
+#pragma unroll
+    for (int j = 0; j < PE; ++j) {
+        const int jj = lane + 64 * j;
+        const int32_t av = S.Aval[bca[j] < E ? bca[j] : E];
+        ncv[0][j] = jj < nB && !(bca[j] < nA && av == bv[j]) ? 1 : 0;  // 1 = not shared with A
     }
-    wave_sync();
-    const int n_rep = nA + wave_scan_array(S.nc, S.NC, R);
-
-    // place every boundary of the union
-    for (int i = lane; i < E; i += 64) {
-        const bool live = i < nA;
-        const int cb = count_below_sorted(S.Bval, nB, live ? S.Aval[i] : 0, rb);
-        const int pos = live ? i + S.NC[cb] : cap - 1;
-        S.U[pos] = S.Aval[i];
-        S.rai[pos] = i;
-        S.rbj[pos] = cb;
-        S.posA[live ? i : E] = pos;
+    int32_t ncx[1][PE], nctot[1];
+    strided_scan<1, PE>(ncv, ncx, nctot);
+    const int n_rep = nA + nctot[0];
+#pragma unroll
+    for (int j = 0; j < PE; ++j) {
+        const int jj = lane + 64 * j;
+        if (jj < R)
+            S.NC[jj] = ncx[0][j];
     }
-    wave_sync();
-    for (int j = lane; j < R; j += 64) {
-        const bool live = j < nB;
-        const int ca = S.Bca[j];
-        const bool own = live && S.nc[j];  // a deficit boundary no spill boundary shares
-        const int pos = own ? ca + S.NC[j] : S.posA[ca < E ? ca : E];
-        const int w = own ? pos : cap - 1;
-        S.U[w] = S.Bval[j];
-        S.rai[w] = ca;
-        S.rbj[w] = j;
-        S.posB[live ? j : R] = pos;
-    }
+    if (lane == 0)
+        S.NC[R] = nctot[0];
     wave_sync();
 
-    // replicas, per-expert ranges, header scalars
-    for (int m = lane; m < cap; m += 64) {
-        const bool live = m < n_rep;
-        const int32_t lo = m ? S.U[m - 1] : 0;
-        int i = S.rai[m], j = S.rbj[m];  // stale past n_rep: clamp to keep reads in bounds
-        i = i < 0 ? 0 : (i > E ? E : i);
-        j = j < 0 ? 0 : (j > R ? R : j);
-        int32_t host = S.Brank[j];
-        host = host < 0 ? 0 : (host >= R ? R - 1 : host);
-        const int32_t rso = lo - S.Aexcl[i];
-        const int32_t rrow = S.load[host] + (lo - S.Bexcl[j]);
-        S.rexp[m] = live ? S.Aexp[i] : 0;
-        S.rhost[m] = live ? host : 0;
-        S.rcnt[m] = live ? S.U[m] - lo : 0;
-        S.rso[m] = live ? rso : 0;
-        S.rrow[m] = live ? rrow : 0;
-        S.rdst[m] = live ? host * C + rrow - rso : 0;
+    // place every spill boundary of the union
+    {
+        int32_t ncb[PE];
+#pragma unroll
+        for (int i = 0; i < PE; ++i)
+            ncb[i] = S.NC[cb[i]];
+#pragma unroll
+        for (int i = 0; i < PE; ++i) {
+            const int ii = lane + 64 * i;
+            const bool live = ii < nA;
+            const int pos = live ? ii + ncb[i] : cap - 1;
+            S.U[pos] = avi[i];
+            S.rai[pos] = ii;
+            S.rbj[pos] = cb[i];
+            S.posA[live ? ii : E] = pos;
+        }
     }
-    for (int i = lane; i < E; i += 64) {
-        int e = S.Aexp[i];
-        e = i < nA && e >= 0 && e < E ? e : E;
-        const int f = i ? S.posA[i - 1] + 1 : 0;
-        S.rep_first[e] = f;
-        S.rep_cnt[e] = S.posA[i] - f + 1;
+    wave_sync();
+    // and every deficit boundary no spill boundary shares
+    {
+        int32_t pa[PE];
+#pragma unroll
+        for (int j = 0; j < PE; ++j)
+            pa[j] = S.posA[bca[j] < E ? bca[j] : E];
+#pragma unroll
+        for (int j = 0; j < PE; ++j) {
+            const int jj = lane + 64 * j;
+            const bool live = jj < nB;
+            const bool own = live && ncv[0][j];
+            const int pos = own ? bca[j] + ncx[0][j] : pa[j];
+            const int w = own ? pos : cap - 1;
+            S.U[w] = bv[j];
+            S.rai[w] = bca[j];
+            S.rbj[w] = jj;
+            S.posB[live ? jj : R] = pos;
+        }
+    }
+    wave_sync();
+
+    // ---- replicas, per-expert replica ranges, replicas per rank -----------
+    // The range reads do not depend on the replica stores, so they go first
+    // and their round trip overlaps the replicas'.
+    int32_t ex[PE], pprev[PE], pcur[PE], qprev[PE], qcur[PE];
+#pragma unroll
+    for (int k = 0; k < PE; ++k) {
+        const int kk = lane + 64 * k;
+        const int ic = kk < E ? kk : E, jc = kk < R ? kk : R;
+        ex[k] = S.Aexp[ic];
+        pprev[k] = S.posA[ic > 0 ? ic - 1 : 0];
+        pcur[k] = S.posA[ic];
+        qprev[k] = S.posB[jc > 0 ? jc - 1 : 0];
+        qcur[k] = S.posB[jc];
+    }
+    constexpr int kJ = 2 * PE < 8 ? 2 * PE : 8;  // replica slots per lane and round: cap <= 128 PE
+    for (int m0 = 0; m0 < cap; m0 += 64 * kJ) {
+        int32_t lo[kJ], hi[kJ], ri[kJ], rj[kJ];
+#pragma unroll
+        for (int k = 0; k < kJ; ++k) {
+            const int m = m0 + lane + 64 * k;
+            const int mc = m < cap ? m : cap - 1;
+            lo[k] = S.U[mc > 0 ? mc - 1 : 0];
+            hi[k] = S.U[mc];
+            ri[k] = S.rai[mc];
+            rj[k] = S.rbj[mc];
+        }
+        int32_t host[kJ], aex[kJ], aexp[kJ], bex[kJ];
+#pragma unroll
+        for (int k = 0; k < kJ; ++k) {
+            const int m = m0 + lane + 64 * k;
+            lo[k] = m ? lo[k] : 0;
+            // stale past n_rep: clamp to keep reads in bounds
+            ri[k] = ri[k] < 0 ? 0 : (ri[k] > E ? E : ri[k]);
+            rj[k] = rj[k] < 0 ? 0 : (rj[k] > R ? R : rj[k]);
+            host[k] = S.Brank[rj[k]];
+            aex[k] = S.Aexcl[ri[k]];
+            aexp[k] = S.Aexp[ri[k]];
+            bex[k] = S.Bexcl[rj[k]];
+        }
+        int32_t hl[kJ];
+#pragma unroll
+        for (int k = 0; k < kJ; ++k) {
+            host[k] = host[k] < 0 ? 0 : (host[k] >= R ? R - 1 : host[k]);
+            hl[k] = S.load[host[k]];
+        }
+#pragma unroll
+        for (int k = 0; k < kJ; ++k) {
+            const int m = m0 + lane + 64 * k;
+            if (m < cap) {
+                const bool live = m < n_rep;
+                const int32_t rso = lo[k] - aex[k];
+                const int32_t rrow = hl[k] + (lo[k] - bex[k]);
+                S.rexp[m] = live ? aexp[k] : 0;
+                S.rhost[m] = live ? host[k] : 0;
+                S.rcnt[m] = live ? hi[k] - lo[k] : 0;
+                S.rso[m] = live ? rso : 0;
+                S.rrow[m] = live ? rrow : 0;
+                S.rdst[m] = live ? host[k] * C + rrow - rso : 0;
+            }
+        }
     }
     int most = 0;
-    for (int j = lane; j < R; j += 64) {
-        const int f = j ? S.posB[j - 1] + 1 : 0;
-        const int c = S.posB[j] - f + 1;  // replicas hosted by this rank
-        most = j < nB && c > most ? c : most;
+#pragma unroll
+    for (int k = 0; k < PE; ++k) {
+        const int kk = lane + 64 * k;
+        const int e = kk < nA && ex[k] >= 0 && ex[k] < E ? ex[k] : E;
+        const int f = kk ? pprev[k] + 1 : 0;
+        S.rep_first[e] = f;
+        S.rep_cnt[e] = pcur[k] - f + 1;
+        const int g = kk ? qprev[k] + 1 : 0;
+        const int c = qcur[k] - g + 1;  // replicas hosted by deficit rank kk
+        most = kk < nB && c > most ? c : most;
     }
-    int tmax = 0;
-    for (int e = lane; e < E; e += 64)
-        tmax = S.T[e] > tmax ? S.T[e] : tmax;
-    most = wave_max(most);
-    tmax = wave_max(tmax);
+    most = wave_max_nonneg(most);
+    tmax = wave_max_nonneg(tmax);
     if (lane == 0) {
         S.misc[MOONEP_PLAN_H_N_REP] = n_rep;
         S.misc[MOONEP_PLAN_H_N_SPILL] = nA;
@@ -393,6 +510,7 @@ __device__ void wave_plan(const PlanLds &S, const int32_t *__restrict__ counts, 
 
 }  // namespace
 
+template <int PE, int kSlotGroup>
 __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
     const int32_t *__restrict__ topk, const int32_t *__restrict__ counts,
     const int32_t *__restrict__ seg_base, int64_t nk, int32_t R, int32_t E, int32_t C,
@@ -407,22 +525,102 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
     const int32_t seg = (int32_t)blockIdx.x * kWaves + wid;
     const int32_t cap = E + R;
 
-    // Waves other than 0 fetch their segment's bases while wave 0 plans.
-    int32_t *run = S.run + wid * E;
-    if (seg < nseg)
-        for (int e = lane; e < E; e += 64)
-            run[e] = seg_base[(int64_t)e * nseg + seg];
-    if (wid == 0)
-        wave_plan(S, counts, R, E, C, policy);
+    // Wave 0 loads the expert counts the plan starts from, and the workgroup
+    // waits for them before anything else is loaded, so they do not queue
+    // behind other loads.  Wave 0 then issues no further global loads until
+    // the plan is done; waves 1-3 load, ahead of the plan, the first batch of
+    // keys (the chunks that hold entries) of their own segments and, for
+    // wave 0, into LDS, and the segment bases of the workgroup's four
+    // segments, which sit side by side in each expert's column: one 16-byte
+    // load per expert when the segment count is a multiple of 4.
+    int32_t t[PE];
+    if (wid == 0) {
+#pragma unroll
+        for (int i = 0; i < PE; ++i) {
+            const int e = lane + 64 * i;
+            t[i] = counts[e < E ? e : E - 1];
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the counts are in
+    }
     __syncthreads();
+    const int64_t beg = (int64_t)seg * segw;
+    const int64_t end = beg + segw < nk ? beg + segw : nk;
+    const int32_t seg0 = (int32_t)blockIdx.x * kWaves;  // the workgroup's first segment (wave 0's)
+    const int64_t beg0 = (int64_t)seg0 * segw;
+    const int64_t end0 = beg0 + segw < nk ? beg0 + segw : nk;
+    int32_t keys[kChunkBatch], keys0[kChunkBatch];
+    if (wid != 0 && seg < nseg) {
+#pragma unroll
+        for (int c = 0; c < kChunkBatch; ++c) {
+            const int64_t n = beg + c * 64 + lane;
+            keys[c] = -1;
+            if (beg + c * 64 < end)
+                keys[c] = topk[n < end ? n : end - 1];
+        }
+    }
+    if (wid == 1 && seg0 < nseg) {
+#pragma unroll
+        for (int c = 0; c < kChunkBatch; ++c) {
+            const int64_t n = beg0 + c * 64 + lane;
+            keys0[c] = -1;
+            if (beg0 + c * 64 < end0)
+                keys0[c] = topk[n < end0 ? n : end0 - 1];
+        }
+    }
+    constexpr int kBE = (PE + 2) / 3;  // experts per thread of waves 1-3: E <= 64 PE <= 192 kBE
+    int4 bq[kBE];
+    if (wid != 0 && seg0 < nseg) {
+        const bool vec = (nseg & 3) == 0;  // then seg0 + 3 < nseg and the group is 16-byte aligned
+#pragma unroll
+        for (int k = 0; k < kBE; ++k) {
+            const int e = tid - 64 + (kBlock - 64) * k;
+            const int32_t *col = seg_base + (int64_t)(e < E ? e : E - 1) * nseg;
+            if (vec) {
+                bq[k] = *(const int4 *)(col + seg0);
+            } else {
+                bq[k].x = col[seg0];
+                bq[k].y = col[seg0 + 1 < nseg ? seg0 + 1 : seg0];
+                bq[k].z = col[seg0 + 2 < nseg ? seg0 + 2 : seg0];
+                bq[k].w = col[seg0 + 3 < nseg ? seg0 + 3 : seg0];
+            }
+        }
+    }
+    if (wid == 0) {
+        wave_plan<PE>(S, t, R, E, C, policy);
+    } else if (seg0 < nseg) {
+#pragma unroll
+        for (int k = 0; k < kBE; ++k) {
+            const int e = tid - 64 + (kBlock - 64) * k;
+            if (e < E) {
+                S.run[e] = bq[k].x;  // segment seg0 always exists
+                if (seg0 + 1 < nseg)
+                    S.run[E + e] = bq[k].y;
+                if (seg0 + 2 < nseg)
+                    S.run[2 * E + e] = bq[k].z;
+                if (seg0 + 3 < nseg)
+                    S.run[3 * E + e] = bq[k].w;
+            }
+        }
+        if (wid == 1) {
+#pragma unroll
+            for (int c = 0; c < kChunkBatch; ++c)
+                S.keys0[c * 64 + lane] = keys0[c];
+        }
+    }
+    int32_t *run = S.run + wid * E;
+    __syncthreads();
+    if (wid == 0 && seg < nseg) {
+#pragma unroll
+        for (int c = 0; c < kChunkBatch; ++c)
+            keys[c] = S.keys0[c * 64 + lane];
+    }
 
-    // ---- workgroup 0 stores the plan --------------------------------------
-    if (blockIdx.x == 0) {
-        const PlanLayout pl = plan_layout(E, R);
+    // ---- the plan goes out in three parts, from up to three workgroups -----
+    const int last_wg = (int)gridDim.x - 1;
+    const PlanLayout pl = plan_layout(E, R);
+    if ((int)blockIdx.x == 0) {
         if (tid < 16)
             plan[pl.header + tid] = S.misc[tid];
-        const int nA = S.misc[MOONEP_PLAN_H_N_SPILL];
-        const int nB = S.misc[MOONEP_PLAN_H_N_DEFICIT];
         for (int m = tid; m < cap; m += kBlock) {
             plan[pl.rep_expert + m] = S.rexp[m];
             plan[pl.rep_host + m] = S.rhost[m];
@@ -430,6 +628,9 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
             plan[pl.rep_spill_off + m] = S.rso[m];
             plan[pl.rep_row_off + m] = S.rrow[m];
         }
+    }
+    if ((int)blockIdx.x == (1 < last_wg ? 1 : last_wg)) {
+        const int nA = S.misc[MOONEP_PLAN_H_N_SPILL];
         for (int e = tid; e < E; e += kBlock) {
             const int32_t r = e / (E / R);
             plan[pl.spill + e] = S.spill[e];
@@ -439,6 +640,10 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
             plan[pl.rep_cnt + e] = S.rep_cnt[e];
             plan[pl.exp_rep_list + e] = e < nA ? S.Aexp[e] : 0;
         }
+    }
+    if ((int)blockIdx.x == (2 < last_wg ? 2 : last_wg)) {
+        // every rank's replica range: empty unless the rank hosts replicas
+        const int nB = S.misc[MOONEP_PLAN_H_N_DEFICIT];
         for (int r = tid; r < R; r += kBlock) {
             plan[pl.load + r] = S.load[r];
             plan[pl.rank_rep_first + r] = 0;
@@ -453,65 +658,94 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
     }
 
     // ---- slot assignment: one wave per segment -----------------------------
+    // Chunks of 64 entries go kSlotGroup at a time through each step (4 or 8:
+    // a segment's chunks, up to 8), so the LDS round trips of a group's
+    // chunks overlap.
     if (seg >= nseg)
         return;
-    const int64_t beg = (int64_t)seg * segw;
-    const int64_t end = beg + segw < nk ? beg + segw : nk;
     for (int64_t b0 = beg; b0 < end; b0 += 64 * kChunkBatch) {
-        int32_t keys[kChunkBatch];
+        if (b0 != beg) {
 #pragma unroll
-        for (int c = 0; c < kChunkBatch; ++c) {
-            const int64_t n = b0 + c * 64 + lane;
-            keys[c] = n < end ? topk[n] : -1;
+            for (int c = 0; c < kChunkBatch; ++c) {
+                const int64_t n = b0 + c * 64 + lane;
+                keys[c] = topk[n < end ? n : end - 1];
+            }
         }
 #pragma unroll
-        for (int c = 0; c < kChunkBatch; ++c) {
-            const int64_t n = b0 + c * 64 + lane;
-            const int32_t e = keys[c];
-            const bool in = n < end;
-            const bool ok = in && e >= 0 && e < E;
-            const uint64_t active = ballot(ok);
-            if (active == 0) {
-                if (in)
-                    slot_of[n] = -1;
-                continue;
+        for (int g = 0; g < kChunkBatch; g += kSlotGroup) {
+            if (b0 + (int64_t)g * 64 >= end)
+                break;  // no later chunk of the batch holds entries
+            int32_t ee[kSlotGroup], got[kSlotGroup], pos[kSlotGroup];
+            uint64_t same[kSlotGroup];
+            bool ok[kSlotGroup];
+            int leader[kSlotGroup];
+#pragma unroll
+            for (int u = 0; u < kSlotGroup; ++u) {
+                const int64_t n = b0 + (g + u) * 64 + lane;
+                const int32_t e = keys[g + u];
+                ok[u] = n < end && e >= 0 && e < E;
+                same[u] = match_lanes(e, ballot(ok[u]), nbits);
+                ee[u] = ok[u] ? e : 0;
+                leader[u] = 63 - __builtin_clzll(same[u] | 1ull);
             }
-            const uint64_t same = match_lanes(e, active, nbits);
-            const int ee = ok ? e : 0;
             // The highest lane of each group of equal keys claims the group's
             // positions with one LDS atomic add, which returns the expert's
             // running count; the other lanes of the group read it from that
             // lane.  LDS executes one wave's atomics in issue order, so the
             // chunks need no barrier between them.
-            const int leader = 63 - __builtin_clzll(same | 1ull);
-            int32_t got = 0;
-            if (ok && leader == lane)
-                got = atomicAdd(&run[ee], __popcll(same));
-            const int32_t pos = __shfl(got, leader, 64) + count_below(same);
-            // home destination and replica destination, both computed
-            const int32_t kp = S.keep[ee];
-            const int32_t home = S.home_dst[ee] + pos;
-            const int32_t q = pos - kp;
-            const int32_t f = S.rep_first[ee];
-            const int32_t last = f + S.rep_cnt[ee] - 1;
-            int32_t j = f;
-            // the table reads happen whether or not the entry has a replica, so
-            // the loop costs the same with and without replicas
-            for (int st = search_steps; st >= 0; --st) {
-                const int32_t t = j + (1 << st);
-                const int32_t tt = t <= last ? t : last;  // keep the read in the table
-                const int32_t so = S.rso[tt < 0 ? 0 : tt];
-                j = t <= last && so <= q ? t : j;
+#pragma unroll
+            for (int u = 0; u < kSlotGroup; ++u) {
+                got[u] = 0;
+                if (ok[u] && leader[u] == lane)
+                    got[u] = atomicAdd(&run[ee[u]], __popcll(same[u]));
             }
-            const int32_t rd = S.rdst[j < 0 ? 0 : j];
-            const int32_t dst = pos < kp ? home : rd + q;
-            // dst is in range whenever counts match topk; the check keeps a
-            // mismatched call from writing outside src_of_slot.
-            if (ok && (uint64_t)(uint32_t)dst < (uint64_t)nk) {
-                slot_of[n] = dst;
-                src_of_slot[dst] = (int32_t)n;
-            } else if (in) {
-                slot_of[n] = -1;
+#pragma unroll
+            for (int u = 0; u < kSlotGroup; ++u)
+                pos[u] = __shfl(got[u], leader[u], 64) + count_below(same[u]);
+            // home destination and replica destination, both computed
+            int32_t kp[kSlotGroup], home[kSlotGroup], q[kSlotGroup], last[kSlotGroup], j[kSlotGroup];
+#pragma unroll
+            for (int u = 0; u < kSlotGroup; ++u) {
+                kp[u] = S.keep[ee[u]];
+                home[u] = S.home_dst[ee[u]];
+                j[u] = S.rep_first[ee[u]];
+                last[u] = S.rep_cnt[ee[u]];
+            }
+#pragma unroll
+            for (int u = 0; u < kSlotGroup; ++u) {
+                home[u] += pos[u];
+                q[u] = pos[u] - kp[u];
+                last[u] += j[u] - 1;
+            }
+            // the table reads happen whether or not the entry has a replica, so
+            // the search costs the same with and without replicas
+            for (int st = search_steps; st >= 0; --st) {
+#pragma unroll
+                for (int u = 0; u < kSlotGroup; ++u) {
+                    const int32_t t = j[u] + (1 << st);
+                    const int32_t tt = t <= last[u] ? t : last[u];  // keep the read in the table
+                    const int32_t so = S.rso[tt < 0 ? 0 : tt];
+                    // '&', not '&&': the read stays unconditional, so the
+                    // group's reads are issued together
+                    j[u] = ((t <= last[u]) & (so <= q[u])) ? t : j[u];
+                }
+            }
+            int32_t rd[kSlotGroup];
+#pragma unroll
+            for (int u = 0; u < kSlotGroup; ++u)
+                rd[u] = S.rdst[j[u] < 0 ? 0 : j[u]];
+#pragma unroll
+            for (int u = 0; u < kSlotGroup; ++u) {
+                const int64_t n = b0 + (g + u) * 64 + lane;
+                const int32_t dst = pos[u] < kp[u] ? home[u] : rd[u] + q[u];
+                // dst is in range whenever counts match topk; the check keeps a
+                // mismatched call from writing outside src_of_slot.
+                if (ok[u] && (uint64_t)(uint32_t)dst < (uint64_t)nk) {
+                    slot_of[n] = dst;
+                    src_of_slot[dst] = (int32_t)n;
+                } else if (n < end) {
+                    slot_of[n] = -1;
+                }
             }
         }
     }
@@ -519,38 +753,82 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
 
 size_t plan_lds_bytes(int32_t E, int32_t R) { return plan_lds_words(E, R) * sizeof(int32_t); }
 
+namespace {
+
+// Large E and R need more than the default 64 KiB of dynamic LDS: raise the
+// kernel's limit once per device, to what the largest allowed shape needs,
+// so later calls with other shapes fit as well.
+template <int PE, int G>
+int raise_plan_lds()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return MOONEP_ERR_HIP;
+    static bool raised[64] = {};
+    if (dev < 0 || dev >= 64 || !raised[dev]) {
+        if (hipFuncSetAttribute((const void *)plan_slots_kernel<PE, G>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)plan_lds_bytes(kMaxExperts, kMaxRanks)) != hipSuccess)
+            return MOONEP_ERR_HIP;
+        if (dev >= 0 && dev < 64)
+            raised[dev] = true;
+    }
+    return MOONEP_OK;
+}
+
+template <int PE, int G>
+int run_plan_g(const moonep_shape &s, const WsLayout &w, const int32_t *topk, const int32_t *counts,
+               const int32_t *base, int steps, int32_t policy, int32_t *plan, int32_t *slot_of,
+               int32_t *src_of_slot, hipStream_t st)
+{
+    const size_t lds = plan_lds_bytes(s.E, s.R);
+    if (lds > 65536) {
+        const int rc = raise_plan_lds<PE, G>();
+        if (rc != MOONEP_OK)
+            return rc;
+    }
+    const int blocks = w.nseg > 0 ? (w.nseg + kWaves - 1) / kWaves : 1;
+    hipLaunchKernelGGL((plan_slots_kernel<PE, G>), dim3(blocks), dim3(kBlock), lds, st, topk, counts,
+                       base, w.nk, s.R, s.E, s.S * s.K, w.segw, w.nseg, expert_bits(s.E), steps,
+                       policy, plan, slot_of, src_of_slot);
+    return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
+}
+
+// Chunks per slot group: a segment of up to 256 entries is 4 chunks, a longer
+// one is taken 8 at a time.
+template <int PE>
+int run_plan(const moonep_shape &s, const WsLayout &w, const int32_t *topk, const int32_t *counts,
+             const int32_t *base, int steps, int32_t policy, int32_t *plan, int32_t *slot_of,
+             int32_t *src_of_slot, hipStream_t st)
+{
+    if (w.segw <= 256)
+        return run_plan_g<PE, 4>(s, w, topk, counts, base, steps, policy, plan, slot_of, src_of_slot, st);
+    return run_plan_g<PE, 8>(s, w, topk, counts, base, steps, policy, plan, slot_of, src_of_slot, st);
+}
+
+}  // namespace
+
 int launch_plan(const moonep_shape &s, const int32_t *topk, const int32_t *counts, void *ws,
                 int32_t *plan, int32_t *slot_of, int32_t *src_of_slot, hipStream_t st,
                 int32_t policy)
 {
     const WsLayout w = ws_layout(s);
     const int32_t *base = (const int32_t *)((const char *)ws + w.hist_off);
-    const int blocks = w.nseg > 0 ? (w.nseg + kWaves - 1) / kWaves : 1;
     int steps = 0;
     while ((1 << (steps + 1)) <= s.R)
         ++steps;
-    const size_t lds = plan_lds_bytes(s.E, s.R);
-    if (lds > 65536) {
-        // Large E and R need more than the default 64 KiB of dynamic LDS: raise
-        // the kernel's limit once per device, to what the largest allowed shape
-        // needs, so later calls with other shapes fit as well.
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess)
-            return MOONEP_ERR_HIP;
-        static bool raised[64] = {};
-        if (dev < 0 || dev >= 64 || !raised[dev]) {
-            if (hipFuncSetAttribute((const void *)plan_slots_kernel,
-                                    hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)plan_lds_bytes(kMaxExperts, kMaxRanks)) != hipSuccess)
-                return MOONEP_ERR_HIP;
-            if (dev >= 0 && dev < 64)
-                raised[dev] = true;
-        }
-    }
-    hipLaunchKernelGGL(plan_slots_kernel, dim3(blocks), dim3(kBlock), lds, st, topk, counts, base,
-                       w.nk, s.R, s.E, s.S * s.K, w.segw, w.nseg, expert_bits(s.E), steps, policy,
-                       plan, slot_of, src_of_slot);
-    return hipGetLastError() == hipSuccess ? MOONEP_OK : MOONEP_ERR_HIP;
+    // experts per lane of the planning wave, rounded up to a power of two
+    const int per = (s.E + 63) / 64;
+    if (per <= 1)
+        return run_plan<1>(s, w, topk, counts, base, steps, policy, plan, slot_of, src_of_slot, st);
+    if (per <= 2)
+        return run_plan<2>(s, w, topk, counts, base, steps, policy, plan, slot_of, src_of_slot, st);
+    if (per <= 4)
+        return run_plan<4>(s, w, topk, counts, base, steps, policy, plan, slot_of, src_of_slot, st);
+    if (per <= 8)
+        return run_plan<8>(s, w, topk, counts, base, steps, policy, plan, slot_of, src_of_slot, st);
+    static_assert(kMaxExperts <= 64 * 16, "experts per lane of the planning wave");
+    return run_plan<16>(s, w, topk, counts, base, steps, policy, plan, slot_of, src_of_slot, st);
 }
 
 }  // namespace moonep
