@@ -188,6 +188,38 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ u32x4 load_nt(const u32x4 *p) { return __builtin_nontemporal_load(p); }
 __device__ __forceinline__ void store_nt(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
+// Cross-lane steps on DPP (data-parallel primitives of the VALU): each is one
+// vector instruction with no LDS round trip.  row_shr:n reads lane i - n of
+// the same 16-lane row (zero when that lane is outside the row);
+// row_bcast:15 and row_bcast:31 (gfx9) hand the last lane of row r - 1, or
+// lane 31, to the rows the row mask enables.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118,
+              kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Inclusive sum over lanes 0..l of v, in lane l (every lane of the wave active).
+__device__ __forceinline__ int32_t wave_incl_sum(int32_t v)
+{
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xf, 0xf, true);
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xa, 0xf, false);  // rows 1 and 3
+    v += __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xc, 0xf, false);  // rows 2 and 3
+    return v;
+}
+
+// Largest v over the wave, for v >= 0 (every lane active).
+__device__ __forceinline__ int32_t wave_max_nonneg(int32_t v)
+{
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr1, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr2, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr4, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowShr8, 0xf, 0xf, true));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowBcast15, 0xa, 0xf, false));
+    v = max(v, __builtin_amdgcn_update_dpp(0, v, kDppRowBcast31, 0xc, 0xf, false));
+    return __builtin_amdgcn_readlane(v, 63);
+}
+
 // Exclusive scan over a block of kBlock threads of one int per thread.
 // `tmp` must hold kWaves ints of LDS.  Returns the exclusive prefix; *total
 // receives the block total.
@@ -195,13 +227,7 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *tmp, int *total)
 {
     const int lane = lane_id();
     const int wid = (int)threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d, 64);
-        if (lane >= d)
-            incl += o;
-    }
+    const int incl = wave_incl_sum(v);
     if (lane == 63)
         tmp[wid] = incl;
     __syncthreads();
