@@ -9,7 +9,9 @@
 //            experts into a private LDS histogram (one ballot per key bit
 //            finds the lanes sharing an expert, so the last lane of each
 //            group adds the group size with one LDS atomic: time independent
-//            of how skewed the routing is) and stores it column-wise, [E][nseg].
+//            of how skewed the routing is); the workgroup then stores its
+//            four segments' counts column-wise, [E][nseg], four side by side
+//            per expert.
 //   rs_scan: one workgroup per expert turns its column into exclusive
 //            per-segment bases (the stable start of each segment within the
 //            expert, used by the slot assignment) and the total T_e.  maxvio
@@ -19,7 +21,15 @@
 
 namespace moonep {
 
-__global__ __launch_bounds__(kBlock) void rs_hist_kernel(const int32_t *__restrict__ topk, int64_t nk,
+// Waves (segments) per rs_hist workgroup.  Its counts go out as 16-byte
+// column runs, one per expert and four segments; rs_hist on gfx950, us
+// (sweep / DeepSeek-V3-like / adversarial): 4.3 / 7.8 / 6.6 at 4 waves, 4.5 /
+// 7.5 / 6.4 at 8, 5.5 / 8.9 / 7.7 at 16, against 4.4 / 9.7 / 7.3 for one
+// 4-byte store per expert and segment.
+constexpr int kHistWaves = 4;
+
+template <int HW>
+__global__ __launch_bounds__(HW * 64) void rs_hist_kernel(const int32_t *__restrict__ topk, int64_t nk,
                                                          int32_t E, int32_t segw, int32_t nseg,
                                                          int32_t nbits, int32_t *__restrict__ hist,
                                                          int32_t *__restrict__ ctl,
@@ -35,11 +45,10 @@ __global__ __launch_bounds__(kBlock) void rs_hist_kernel(const int32_t *__restri
         maxvio[0] = 0.0f;  // the start of rs_scan's atomic max, which runs after this launch
     __syncthreads();
 
-    const int32_t seg = (int32_t)blockIdx.x * kWaves + wid;
-    if (seg >= nseg)
-        return;
+    const int32_t seg0 = (int32_t)blockIdx.x * HW;  // the workgroup's first segment
+    const int32_t seg = seg0 + wid;
     const int64_t beg = (int64_t)seg * segw;
-    const int64_t end = beg + segw < nk ? beg + segw : nk;
+    const int64_t end = seg < nseg ? (beg + segw < nk ? beg + segw : nk) : beg;  // none past nseg
     bool bad = false;
     for (int64_t b0 = beg; b0 < end; b0 += 64 * kChunkBatch) {
         int32_t keys[kChunkBatch];
@@ -65,9 +74,25 @@ __global__ __launch_bounds__(kBlock) void rs_hist_kernel(const int32_t *__restri
     }
     if (ballot(bad) != 0 && lane == 0)
         atomicCAS(&ctl[kCtlError], 0, (int32_t)MOONEP_DEV_BAD_EXPERT_ID);
-    wave_sync();
-    for (int e = lane; e < E; e += 64)
-        hist[(int64_t)e * nseg + seg] = h[e];
+    __syncthreads();
+    // The workgroup's HW segments sit side by side in each expert's column:
+    // 16-byte stores, HW / 4 per expert, when the segment count is a multiple
+    // of HW (then all of them exist and the run is 16-byte aligned).
+    const bool vec = nseg % HW == 0;
+    for (int e = (int)threadIdx.x; e < E; e += HW * 64) {
+        int32_t *col = hist + (int64_t)e * nseg + seg0;
+        if (vec) {
+#pragma unroll
+            for (int q = 0; q < HW / 4; ++q)
+                *(int4 *)(col + 4 * q) = make_int4(lds[(4 * q) * E + e], lds[(4 * q + 1) * E + e],
+                                                   lds[(4 * q + 2) * E + e], lds[(4 * q + 3) * E + e]);
+        } else {
+#pragma unroll
+            for (int w = 0; w < HW; ++w)
+                if (seg0 + w < nseg)
+                    col[w] = lds[w * E + e];
+        }
+    }
 }
 
 // maxvio = fp32((Tmax*E)/nk - 1) is the largest of the experts' fp32((T_e*E)/nk
@@ -154,10 +179,10 @@ int launch_route_stats(const moonep_shape &s, const int32_t *topk, int32_t *coun
     int32_t *ctl = (int32_t *)ws;
     int32_t *hist = (int32_t *)((char *)ws + w.hist_off);
     if (w.nseg > 0) {
-        const int blocks = (w.nseg + kWaves - 1) / kWaves;
-        const size_t lds = (size_t)kWaves * s.E * sizeof(int32_t);
-        hipLaunchKernelGGL(rs_hist_kernel, dim3(blocks), dim3(kBlock), lds, st, topk, w.nk, s.E,
-                           w.segw, w.nseg, expert_bits(s.E), hist, ctl, maxvio);
+        const int blocks = (w.nseg + kHistWaves - 1) / kHistWaves;
+        const size_t lds = (size_t)kHistWaves * s.E * sizeof(int32_t);
+        hipLaunchKernelGGL(rs_hist_kernel<kHistWaves>, dim3(blocks), dim3(kHistWaves * 64), lds, st, topk,
+                           w.nk, s.E, w.segw, w.nseg, expert_bits(s.E), hist, ctl, maxvio);
     }
     hipLaunchKernelGGL(rs_scan_kernel, dim3(s.E), dim3(kBlock), 0, st, hist, w.nseg, s.E, w.nk,
                        counts, maxvio);
