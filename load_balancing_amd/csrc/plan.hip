@@ -231,29 +231,44 @@ __device__ void wave_plan(const PlanLds &S, int32_t (&t)[PE], int32_t R, int32_t
     }
     // what the experts taken before e hold: the prefix of the rank's counts
     // (lowest id first), or the sum of the rank's counts ordered before e by
-    // (count descending, id ascending)
+    // (count descending, id ascending), read kLW of the rank's counts at a
+    // time for all of the lane's experts together
+    int32_t before[PE];
+#pragma unroll
+    for (int i = 0; i < PE; ++i)
+        before[i] = p[0][i] - prs[i];
+    if (policy == 1) {
+        constexpr int kLW = PE <= 4 ? 8 : 32 / PE;
+#pragma unroll
+        for (int i = 0; i < PE; ++i)
+            before[i] = 0;
+        for (int32_t k0 = 0; k0 < Lx; k0 += kLW) {
+            int32_t tk[PE][kLW];
+#pragma unroll
+            for (int i = 0; i < PE; ++i) {
+                const int32_t k1 = (lane + 64 * i < E ? lane + 64 * i : E - 1) / Lx * Lx;
+#pragma unroll
+                for (int u = 0; u < kLW; ++u)
+                    tk[i][u] = S.T[k1 + (k0 + u < Lx ? k0 + u : Lx - 1)];
+            }
+#pragma unroll
+            for (int i = 0; i < PE; ++i) {
+                const int e = lane + 64 * i;
+                const int32_t k1 = (e < E ? e : E - 1) / Lx * Lx;
+#pragma unroll
+                for (int u = 0; u < kLW; ++u) {
+                    const int32_t k = k1 + k0 + u;
+                    const bool first = tk[i][u] > t[i] || (tk[i][u] == t[i] && k < e);
+                    before[i] += k0 + u < Lx && first ? tk[i][u] : 0;
+                }
+            }
+        }
+    }
 #pragma unroll
     for (int i = 0; i < PE; ++i) {
         const int e = lane + 64 * i;
         const int32_t excess = (pre[i] - prs[i]) - C;
-        int32_t before = p[0][i] - prs[i];
-        if (policy == 1) {
-            const int32_t te = t[i];
-            const int32_t k1 = (e < E ? e : E - 1) / Lx * Lx, kend = k1 + Lx;
-            before = 0;
-            for (int32_t k0 = k1; k0 < kend; k0 += 8) {
-                int32_t tk[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-                    tk[u] = S.T[k0 + u < kend ? k0 + u : kend - 1];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    const int32_t k = k0 + u;
-                    before += k < kend && (tk[u] > te || (tk[u] == te && k < e)) ? tk[u] : 0;
-                }
-            }
-        }
-        int32_t give = excess - before;
+        int32_t give = excess - before[i];
         give = give < 0 ? 0 : (give > t[i] ? t[i] : give);
         give = excess > 0 && e < E ? give : 0;
         sc[0][i] = give;
