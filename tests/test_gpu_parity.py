@@ -383,6 +383,36 @@ def test_plan_random_shapes(largest_first):
             np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot, err_msg=msg)
 
 
+# Many experts per lane of the planning wave (E = 512 and 1024: 8 and 16 per
+# lane) with 1M routed entries, so each wave's segment is 512 entries and the
+# slot loop takes its chunks 8 at a time.
+WIDE_LONG = [
+    synth.Workload("wide8_long", 32, 512, 4096, 8, 8, "zipf", alpha=1.2),
+    synth.Workload("wide16_long", 16, 1024, 8192, 8, 8, "zipf", alpha=1.0),
+]
+
+
+@pytest.mark.parametrize("largest_first", [False, True], ids=["lowest_id", "largest_first"])
+@pytest.mark.parametrize("w", WIDE_LONG, ids=lambda w: w.name)
+def test_plan_many_experts_per_lane_long_segments(w, largest_first):
+    """Counts, maxvio, every plan field and both slot maps, bit-exact against
+    the oracle, for both planners."""
+    assert w.NK >= 1 << 20 and w.E > 256
+    policy = oracle.PLAN_LARGEST_FIRST if largest_first else oracle.PLAN_LOWEST_ID
+    topk, _ = synth.routing(w, 0)
+    T, mv, pl, slot_of, src_of_slot = oracle_plan(w, topk, policy)
+    assert pl.n_rep > 0
+    b = mx.allocate(shape_of(w))
+    mx.plan_step(b, to_dev(topk), largest_first=largest_first)
+    torch.cuda.synchronize()
+    assert mx.moonep_read_error(b.workspace) == mx.DEV_OK
+    np.testing.assert_array_equal(b.expert_counts.cpu().numpy(), T)
+    assert b.maxvio.item() == mv
+    compare_plan(b.plan_fields(), pl, w.E, w.R)
+    np.testing.assert_array_equal(b.slot_of.cpu().numpy(), slot_of)
+    np.testing.assert_array_equal(b.src_of_slot.cpu().numpy(), src_of_slot)
+
+
 @pytest.mark.parametrize("w", [synth.WORKLOADS["tiny"]] + [e for e in EDGE if e.name in (
     "ragged", "heavy_skew", "k9", "adversarial_small")] + LIMITS[:2], ids=lambda w: w.name)
 def test_whole_chain_largest_first(w):
