@@ -324,9 +324,10 @@ __device__ void wave_plan(const PlanLds &S, int32_t (&t)[PE], int32_t R, int32_t
     // ---- the union of both lists' running totals -------------------------
     // Two searches of fixed depth, run side by side: each deficit total's
     // place among the spill totals (bca) and each spill total's among the
-    // deficit totals (cb).  Both take the depth of the E-entry list; the
-    // extra steps of the shorter list's search change nothing (2^ea > E >= R).
-    const int ea = ceil_log2(E + 1);
+    // deficit totals (cb).  Both lists hold fewer than E entries (nA <= E - 1,
+    // nB <= R - 1), so 2^ea >= E covers both; the extra steps of the shorter
+    // list's search change nothing.
+    const int ea = ceil_log2(E);
     int32_t bv[PE], bca[PE], avi[PE], cb[PE], ncv[1][PE];
 #pragma unroll
     for (int k = 0; k < PE; ++k) {
@@ -598,33 +599,42 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
             keys[c] = S.keys0[c * 64 + lane];
     }
 
-    // ---- the plan goes out in three parts, from up to three workgroups -----
+    // ---- the plan goes out in five parts, from up to five workgroups -------
     const int last_wg = (int)gridDim.x - 1;
     const PlanLayout pl = plan_layout(E, R);
-    if ((int)blockIdx.x == 0) {
+    auto stores_part = [&](int part) { return (int)blockIdx.x == (part < last_wg ? part : last_wg); };
+    if (stores_part(0)) {
         if (tid < 16)
             plan[pl.header + tid] = S.misc[tid];
         for (int m = tid; m < cap; m += kBlock) {
             plan[pl.rep_expert + m] = S.rexp[m];
             plan[pl.rep_host + m] = S.rhost[m];
+        }
+    }
+    if (stores_part(3)) {
+        for (int m = tid; m < cap; m += kBlock) {
             plan[pl.rep_count + m] = S.rcnt[m];
             plan[pl.rep_spill_off + m] = S.rso[m];
             plan[pl.rep_row_off + m] = S.rrow[m];
         }
     }
-    if ((int)blockIdx.x == (1 < last_wg ? 1 : last_wg)) {
-        const int nA = S.misc[MOONEP_PLAN_H_N_SPILL];
+    if (stores_part(1)) {
         for (int e = tid; e < E; e += kBlock) {
             const int32_t r = e / (E / R);
             plan[pl.spill + e] = S.spill[e];
             plan[pl.keep + e] = S.keep[e];
             plan[pl.home_row_off + e] = S.home_dst[e] - r * C;
+        }
+    }
+    if (stores_part(4)) {
+        const int nA = S.misc[MOONEP_PLAN_H_N_SPILL];
+        for (int e = tid; e < E; e += kBlock) {
             plan[pl.rep_first + e] = S.rep_first[e];
             plan[pl.rep_cnt + e] = S.rep_cnt[e];
             plan[pl.exp_rep_list + e] = e < nA ? S.Aexp[e] : 0;
         }
     }
-    if ((int)blockIdx.x == (2 < last_wg ? 2 : last_wg)) {
+    if (stores_part(2)) {
         // every rank's replica range: empty unless the rank hosts replicas
         const int nB = S.misc[MOONEP_PLAN_H_N_DEFICIT];
         for (int r = tid; r < R; r += kBlock) {
@@ -667,10 +677,22 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
                 const int64_t n = b0 + (g + u) * 64 + lane;
                 const int32_t e = keys[g + u];
                 ok[u] = n < end && e >= 0 && e < E;
-                same[u] = match_lanes(e, ballot(ok[u]), nbits);
+                same[u] = ballot(ok[u]);
                 ee[u] = ok[u] ? e : 0;
-                leader[u] = 63 - __builtin_clzll(same[u] | 1ull);
             }
+            // lanes with an equal key: one ballot per key bit, the group's
+            // chunks side by side so that their chains interleave
+            for (int bit = 0; bit < nbits; ++bit) {
+#pragma unroll
+                for (int u = 0; u < kSlotGroup; ++u) {
+                    const bool on = (ee[u] >> bit) & 1;
+                    const uint64_t set = ballot(on);
+                    same[u] &= on ? set : ~set;
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < kSlotGroup; ++u)
+                leader[u] = 63 - __builtin_clzll(same[u] | 1ull);
             // The highest lane of each group of equal keys claims the group's
             // positions with one LDS atomic add, which returns the expert's
             // running count; the other lanes of the group read it from that
