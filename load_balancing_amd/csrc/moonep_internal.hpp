@@ -120,17 +120,21 @@ __device__ __forceinline__ void wave_sync()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Lanes (within `active`) whose key equals this lane's key: one ballot per
-// key bit, so the cost does not depend on how the keys repeat.
-__device__ __forceinline__ uint64_t match_lanes(int32_t key, uint64_t active, int nbits)
+// For G chunks of keys at once: narrows same[u], which enters as the mask of
+// lanes that take part in chunk u, to those whose key equals this lane's.
+// One ballot per key bit, so the cost does not depend on how the keys
+// repeat; the G chunks' chains run side by side.
+template <int G>
+__device__ __forceinline__ void match_lanes(const int32_t (&key)[G], int nbits, uint64_t (&same)[G])
 {
-    uint64_t m = active;
     for (int b = 0; b < nbits; ++b) {
-        const bool bit = (key >> b) & 1;
-        const uint64_t set = ballot(bit);
-        m &= bit ? set : ~set;
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            const bool on = (key[u] >> b) & 1;
+            const uint64_t set = ballot(on);
+            same[u] &= on ? set : ~set;
+        }
     }
-    return m;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }

@@ -680,16 +680,7 @@ __global__ __launch_bounds__(kBlock) void plan_slots_kernel(
                 same[u] = ballot(ok[u]);
                 ee[u] = ok[u] ? e : 0;
             }
-            // lanes with an equal key: one ballot per key bit, the group's
-            // chunks side by side so that their chains interleave
-            for (int bit = 0; bit < nbits; ++bit) {
-#pragma unroll
-                for (int u = 0; u < kSlotGroup; ++u) {
-                    const bool on = (ee[u] >> bit) & 1;
-                    const uint64_t set = ballot(on);
-                    same[u] &= on ? set : ~set;
-                }
-            }
+            match_lanes(ee, nbits, same);  // lanes with an equal key
 #pragma unroll
             for (int u = 0; u < kSlotGroup; ++u)
                 leader[u] = 63 - __builtin_clzll(same[u] | 1ull);

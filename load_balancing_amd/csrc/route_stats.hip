@@ -27,6 +27,7 @@ namespace moonep {
 // 7.5 / 6.4 at 8, 5.5 / 8.9 / 7.7 at 16, against 4.4 / 9.7 / 7.3 for one
 // 4-byte store per expert and segment.
 constexpr int kHistWaves = 4;
+constexpr int kGroup = 4;  // 64-entry chunks matched side by side
 
 template <int HW>
 __global__ __launch_bounds__(HW * 64) void rs_hist_kernel(const int32_t *__restrict__ topk, int64_t nk,
@@ -57,19 +58,29 @@ __global__ __launch_bounds__(HW * 64) void rs_hist_kernel(const int32_t *__restr
             const int64_t n = b0 + c * 64 + lane;
             keys[c] = n < end ? topk[n] : -1;
         }
+        // chunks kGroup at a time, their key matching side by side
 #pragma unroll
-        for (int c = 0; c < kChunkBatch; ++c) {
-            const int64_t n = b0 + c * 64 + lane;
-            const int32_t e = keys[c];
-            const bool in = n < end;
-            const bool ok = in && e >= 0 && e < E;
-            bad |= in && !ok;
-            const uint64_t active = ballot(ok);
-            if (active == 0)
-                continue;
-            const uint64_t same = match_lanes(e, active, nbits);
-            if (ok && (same >> lane) == 1ull)  // highest lane of its group
-                atomicAdd(&h[e], __popcll(same));  // LDS; no barrier between chunks
+        for (int g = 0; g < kChunkBatch; g += kGroup) {
+            if (b0 + (int64_t)g * 64 >= end)
+                break;  // no later chunk of the batch holds entries
+            int32_t ee[kGroup];
+            bool ok[kGroup];
+            uint64_t same[kGroup];
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u) {
+                const int64_t n = b0 + (g + u) * 64 + lane;
+                const int32_t e = keys[g + u];
+                const bool in = n < end;
+                ok[u] = in && e >= 0 && e < E;
+                bad |= in && !ok[u];
+                ee[u] = ok[u] ? e : 0;
+                same[u] = ballot(ok[u]);
+            }
+            match_lanes(ee, nbits, same);  // lanes with an equal key
+#pragma unroll
+            for (int u = 0; u < kGroup; ++u)
+                if (ok[u] && (same[u] >> lane) == 1ull)  // highest lane of its group
+                    atomicAdd(&h[ee[u]], __popcll(same[u]));  // LDS; no barrier between chunks
         }
     }
     if (ballot(bad) != 0 && lane == 0)
