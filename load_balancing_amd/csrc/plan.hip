@@ -44,7 +44,7 @@ struct PlanLds {
     // spill list (A), index i < nA
     int32_t *Aval, *Aexp, *Aexcl, *posA;
     // per rank / deficit list (B), index j < nB
-    int32_t *load, *Bval, *Brank, *Bexcl, *NC, *posB;
+    int32_t *load, *Bval, *Brank, *Brow, *NC, *posB;  // Brow: first replica row base (load - Dp)
     // per replica (plan order)
     int32_t *U, *rai, *rbj, *rexp, *rhost, *rcnt, *rso, *rrow, *rdst;
     int32_t *misc;  // [16]: scalars of the plan header
@@ -73,7 +73,7 @@ __device__ inline PlanLds carve(int32_t *base, int32_t E, int32_t R)
         *a = p;
         p += e1;
     }
-    int32_t **r_arrays[kRArrays] = {&L.load, &L.Bval, &L.Brank, &L.Bexcl, &L.NC, &L.posB};
+    int32_t **r_arrays[kRArrays] = {&L.load, &L.Bval, &L.Brank, &L.Brow, &L.NC, &L.posB};
     for (int32_t **a : r_arrays) {
         *a = p;
         p += r1;
@@ -220,14 +220,15 @@ __device__ void wave_plan(const PlanLds &S, int32_t (&t)[PE], int32_t R, int32_t
         pre[i] = S.P[(r + 1) * Lx];
     }
     int32_t sc[4][PE];  // spill, spill flag (per expert); deficit, deficit flag (per rank)
+    int32_t ld[PE];     // rank loads
 #pragma unroll
     for (int j = 0; j < PE; ++j) {
         const int r = lane + 64 * j;
-        const int32_t ld = rb[j] - ra[j];
+        ld[j] = rb[j] - ra[j];
         if (r < R)
-            S.load[r] = ld;
-        sc[2][j] = r < R && ld < C ? C - ld : 0;
-        sc[3][j] = r < R && ld < C ? 1 : 0;
+            S.load[r] = ld[j];
+        sc[2][j] = r < R && ld[j] < C ? C - ld[j] : 0;
+        sc[3][j] = r < R && ld[j] < C ? 1 : 0;
     }
     // what the experts taken before e hold: the prefix of the rank's counts
     // (lowest id first), or the sum of the rank's counts ordered before e by
@@ -317,7 +318,9 @@ __device__ void wave_plan(const PlanLds &S, int32_t (&t)[PE], int32_t R, int32_t
         const int b = r < R && sc[2][j] > 0 ? sx[3][j] : R;
         S.Bval[b] = sx[2][j] + sc[2][j];
         S.Brank[b] = r;
-        S.Bexcl[b] = sx[2][j];
+        // a replica that starts at union value lo on this rank starts at row
+        // load + (lo - the deficits before this rank) of its buffer
+        S.Brow[b] = ld[j] - sx[2][j];
     }
     wave_sync();
 
@@ -429,7 +432,7 @@ __device__ void wave_plan(const PlanLds &S, int32_t (&t)[PE], int32_t R, int32_t
             ri[k] = S.rai[mc];
             rj[k] = S.rbj[mc];
         }
-        int32_t host[kJ], aex[kJ], aexp[kJ], bex[kJ];
+        int32_t host[kJ], aex[kJ], aexp[kJ], brow[kJ];
 #pragma unroll
         for (int k = 0; k < kJ; ++k) {
             const int m = m0 + lane + 64 * k;
@@ -440,21 +443,16 @@ __device__ void wave_plan(const PlanLds &S, int32_t (&t)[PE], int32_t R, int32_t
             host[k] = S.Brank[rj[k]];
             aex[k] = S.Aexcl[ri[k]];
             aexp[k] = S.Aexp[ri[k]];
-            bex[k] = S.Bexcl[rj[k]];
-        }
-        int32_t hl[kJ];
-#pragma unroll
-        for (int k = 0; k < kJ; ++k) {
-            host[k] = host[k] < 0 ? 0 : (host[k] >= R ? R - 1 : host[k]);
-            hl[k] = S.load[host[k]];
+            brow[k] = S.Brow[rj[k]];
         }
 #pragma unroll
         for (int k = 0; k < kJ; ++k) {
             const int m = m0 + lane + 64 * k;
             if (m < cap) {
                 const bool live = m < n_rep;
+                host[k] = host[k] < 0 ? 0 : (host[k] >= R ? R - 1 : host[k]);
                 const int32_t rso = lo[k] - aex[k];
-                const int32_t rrow = hl[k] + (lo[k] - bex[k]);
+                const int32_t rrow = brow[k] + lo[k];
                 S.rexp[m] = live ? aexp[k] : 0;
                 S.rhost[m] = live ? host[k] : 0;
                 S.rcnt[m] = live ? hi[k] - lo[k] : 0;
@@ -810,8 +808,11 @@ int launch_plan(const moonep_shape &s, const int32_t *topk, const int32_t *count
 {
     const WsLayout w = ws_layout(s);
     const int32_t *base = (const int32_t *)((const char *)ws + w.hist_off);
-    int steps = 0;
-    while ((1 << (steps + 1)) <= s.R)
+    // Depth of the slot loop's replica search: an expert's replicas sit on
+    // distinct deficit ranks, at most R - 1 of them, so the search covers
+    // offsets 0 .. R - 2 from its first replica: 2^(steps + 1) >= R - 1.
+    int steps = -1;
+    while ((1 << (steps + 1)) < s.R - 1)
         ++steps;
     // experts per lane of the planning wave, rounded up to a power of two
     const int per = (s.E + 63) / 64;
