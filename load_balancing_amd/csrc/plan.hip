@@ -20,9 +20,10 @@
 //
 // The plan is O(E + R) work.  Every workgroup computes it redundantly in LDS
 // (no grid-wide barrier, no second launch), with wave 0 alone doing the work
-// through wave-level scans -- 64 lanes, each owning a contiguous run of
-// experts or ranks, with no workgroup barrier until the plan is done.
-// Workgroup 0 stores it.  Then each wave assigns the entries of one segment:
+// (see wave_plan: lane l owns experts and ranks l, l + 64, ... in registers,
+// scans run on DPP) and no workgroup barrier until the plan is done, while
+// the other waves load keys and segment bases.  Five workgroups store it.
+// Then each wave assigns the entries of one segment:
 //   pos = (entries of the same expert in earlier segments)  -- from rs_scan
 //       + (entries of the same expert earlier in this segment) -- a running
 //         per-wave LDS counter plus the lane's rank among equal keys of its
@@ -30,7 +31,8 @@
 //   pos < keep_e -> home row, else the replica whose spill range holds
 //   pos - keep_e (binary search of fixed depth).  Every lane computes both
 //   and selects, so the time does not depend on how much of the routing
-//   spills.
+//   spills.  A wave takes its 64-entry chunks 4 or 8 at a time through each
+//   of these steps, so that the LDS round trips of a group overlap.
 #include "moonep_internal.hpp"
 
 namespace moonep {
