@@ -39,12 +39,12 @@ __global__ __launch_bounds__(HW * 64) void rs_hist_kernel(const int32_t *__restr
     extern __shared__ int32_t lds[];
     const int wid = (int)threadIdx.x >> 6;
     const int lane = lane_id();
-    int32_t *h = lds + wid * E;
+    int32_t *h = lds + wid * E;  // this wave's own histogram: no workgroup barrier until the stores
     for (int e = lane; e < E; e += 64)
         h[e] = 0;
     if (blockIdx.x == 0 && threadIdx.x == 0)
         maxvio[0] = 0.0f;  // the start of rs_scan's atomic max, which runs after this launch
-    __syncthreads();
+    wave_sync();
 
     const int32_t seg0 = (int32_t)blockIdx.x * HW;  // the workgroup's first segment
     const int32_t seg = seg0 + wid;
