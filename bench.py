@@ -458,6 +458,94 @@ def map_study(reps=5, seed=0):
                       "cache": "untimed 512 MiB read before each call"}), flush=True)
 
 
+def ceilings(reps=9):
+    """Machine ceilings on this GPU, from libmoonep_ceilings.so (kernels of
+    their own, outside libmoonep): 1 GiB non-temporal streams (copy, read-only,
+    write-only) from an evicted cache, the best of 64-, 128- and 256-thread
+    workgroups at 1-32 waves per CU;
+    the bf16 matrix pipe (32x32x16 MFMAs on
+    register operands, 8 independent accumulators per wave, no memory
+    traffic) at 1 and 4 waves per SIMD; and LDS-DMA (16-byte global_load_lds)
+    from a 2 MiB buffer that stays in the L2, 8 or 16 waves per CU, 8 KiB per
+    wave in flight.  Median of `reps` launches each, HIP events on the launching
+    stream.  Prints one JSON line."""
+    import ctypes
+
+    import torch
+
+    from load_balancing_amd import build as hip_build
+
+    path = hip_build.CEIL_LIB
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
+    L = ctypes.CDLL(path)
+    VP, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    L.ceil_stream.argtypes = [VP, VP, I64, I, I, I, VP, VP]
+    L.ceil_mfma.argtypes = [I, I, VP, VP]
+    L.ceil_lds_dma.argtypes = [VP, I64, I, I, VP, VP]
+    dev = torch.device("cuda:0")
+    st = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(st.cuda_stream)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    flush_buf = torch.ones(1 << 27, dtype=torch.float32, device=dev)
+
+    def timed(fn, flush):
+        ts = []
+        for _ in range(reps):
+            if flush:
+                flush_buf.sum()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            rc = fn()
+            e1.record(st)
+            assert rc == 0, rc
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        return sorted(ts)[reps // 2]
+
+    out = {}
+    nbytes = 1 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.empty(cus * 32 * 64, dtype=torch.int32, device=dev)  # one word per thread
+    nvec = nbytes // 16
+    for mode, name, moved in ((0, "copy", 2 * nbytes), (1, "read", nbytes), (2, "write", nbytes)):
+        best = None
+        for block in (64, 128, 256):
+            for waves_per_cu in (1, 2, 4, 8, 16, 32):  # the best configuration is reported
+                g = cus * waves_per_cu * 64 // block
+                if g < cus:
+                    continue
+                t = timed(lambda: L.ceil_stream(src.data_ptr(), dst.data_ptr(), nvec, mode, g, block,
+                                                sink.data_ptr(), sp), True)
+                if best is None or t < best[0]:
+                    best = (t, block, waves_per_cu)
+        out[f"hbm_{name}_GBps"] = round(moved / best[0] / 1e9, 1)
+        out[f"hbm_{name}_config"] = f"{best[1]}-thread workgroups, {best[2]} waves per CU"
+    del src, dst
+    chains = L.ceil_mfma_chains()
+    iters = 4096
+    for waves_per_simd in (1, 4):
+        g = cus * waves_per_simd  # 256-thread workgroups: one wave per SIMD each
+        res = torch.empty(g * 256, dtype=torch.float32, device=dev)
+        t = timed(lambda: L.ceil_mfma(g, iters, res.data_ptr(), sp), False)
+        flops = g * 4 * iters * chains * 32 * 32 * 16 * 2
+        out[f"mfma_bf16_TFLOPs_{waves_per_simd}_wave_per_simd"] = round(flops / t / 1e12, 1)
+    chunks = 2048  # 2 MiB
+    buf = torch.ones(chunks * 256, dtype=torch.int32, device=dev)
+    loads, waves = L.ceil_lds_dma_loads(), L.ceil_lds_dma_waves()
+    dma_iters = 2048
+    for per_cu in (1, 2):  # 512-thread workgroups with 64 KiB of LDS: at most 2 per CU
+        g = cus * per_cu
+        res = torch.empty(g * waves, dtype=torch.int32, device=dev)
+        L.ceil_lds_dma(buf.data_ptr(), chunks, g, 16, res.data_ptr(), sp)  # brings the buffer into the L2s
+        t = timed(lambda: L.ceil_lds_dma(buf.data_ptr(), chunks, g, dma_iters, res.data_ptr(), sp), False)
+        out[f"lds_dma_from_l2_GBps_{per_cu}_workgroup_per_cu"] = round(
+            g * waves * dma_iters * loads * 1024 / t / 1e9, 1)
+    out["peaks"] = {"hbm_GBps": 8000.0, "mfma_bf16_TFLOPs": 2500.0}
+    print(json.dumps({"ceilings": out, "reps": reps, "cus": cus}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -481,9 +569,15 @@ def main():
     ap.add_argument("--map-study", action="store_true",
                     help="diagnostic: time the movers over non-plan destination maps (identity, "
                          "uniform expert, random permutation) beside two plans, then exit")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="diagnostic: measure the machine ceilings (HBM streams, the bf16 matrix "
+                         "pipe, LDS-DMA from the L2) with libmoonep_ceilings.so, then exit")
     args = ap.parse_args()
     if args.map_study:
         map_study()
+        return
+    if args.ceilings:
+        ceilings()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark measures one GPU: R logical ranks are slices of one "

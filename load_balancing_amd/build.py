@@ -1,4 +1,4 @@
-"""Build libmoonep.so (gfx950) in-tree with hipcc.
+"""Build libmoonep.so and libmoonep_ceilings.so (gfx950) in-tree with hipcc.
 
     python -m load_balancing_amd.build
 """
@@ -23,9 +23,15 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+# The machine-ceiling microbenchmarks (bench.py --ceilings): a library of
+# their own, outside libmoonep's C-ABI.
+CEIL_LIB = os.path.join(HERE, "libmoonep_ceilings.so")
+CEIL_SOURCES = ["ceilings.hip"]
+
+
+def _hipcc(sources, out, verbose):
     cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC,
-           *[os.path.join(CSRC, s) for s in SOURCES], "-o", LIB + ".tmp"]
+           *[os.path.join(CSRC, s) for s in sources], "-o", out + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -35,8 +41,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(LIB + ".tmp", LIB)
-    return LIB
+    os.replace(out + ".tmp", out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """The ceilings library, then libmoonep.so; returns the path of libmoonep.so."""
+    _hipcc(CEIL_SOURCES, CEIL_LIB, verbose)
+    return _hipcc(SOURCES, LIB, verbose)
 
 
 if __name__ == "__main__":

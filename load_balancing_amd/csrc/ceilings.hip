@@ -1,0 +1,167 @@
+// ceilings.hip -- microbenchmarks of the machine ceilings the kernels are
+// judged against: HBM streams (copy, read-only, write-only), the matrix
+// pipe's bf16 rate, and LDS-DMA from data that sits in the L2.  Built as its
+// own library (libmoonep_ceilings.so), outside the C-ABI of libmoonep.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ u32x4 load_nt(const u32x4 *p) { return __builtin_nontemporal_load(p); }
+__device__ __forceinline__ void store_nt(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
+
+// mode 0: dst = src; mode 1: read src, one word per thread to sink; mode 2:
+// write dst.  16-byte non-temporal vectors, grid-stride, kUnroll vectors per
+// thread in flight (all loads of a round issued before its stores).
+constexpr int kUnroll = 4;
+
+__global__ __launch_bounds__(256) void stream_kernel(const u32x4 *__restrict__ src,
+                                                     u32x4 *__restrict__ dst, int64_t n,
+                                                     int mode, uint32_t *__restrict__ sink)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint32_t acc = 0;
+    for (int64_t i = i0; i < n; i += kUnroll * stride) {
+        u32x4 v[kUnroll];
+        if (mode != 2) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t j = i + u * stride;
+                v[u] = j < n ? load_nt(src + j) : u32x4{0u, 0u, 0u, 0u};
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                v[u] = u32x4{(uint32_t)i, (uint32_t)u, 2u, 3u};
+        }
+        if (mode == 1) {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u)
+                acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        } else {
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t j = i + u * stride;
+                if (j < n)
+                    store_nt(dst + j, v[u]);
+            }
+        }
+    }
+    if (mode == 1)
+        sink[i0] = acc;  // sink holds one word per launched thread
+}
+
+// kChains independent 32x32x16 bf16 MFMA accumulators per wave, `iters`
+// rounds; operands come from the thread id so nothing folds.  One float per
+// thread goes to out.
+constexpr int kChains = 8;
+
+__global__ __launch_bounds__(256) void mfma_kernel(int iters, float *__restrict__ out)
+{
+    const int tid = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    bf16x8 a, b;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        a[j] = (__bf16)(float)((tid + j) & 7);
+        b[j] = (__bf16)(float)((tid * 3 + j) & 7);
+    }
+    f32x16 acc[kChains];
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            acc[c][r] = 0.0f;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int c = 0; c < kChains; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[c], 0, 0, 0);
+    }
+    float s = 0.0f;
+#pragma unroll
+    for (int c = 0; c < kChains; ++c)
+        s += acc[c][c];
+    out[tid] = s;
+}
+
+// LDS-DMA (global_load_lds_dwordx4) from a buffer that stays in the L2: each
+// wave loads kDmaLoads KiB per round into its own LDS region (one KiB per
+// load: 64 lanes x 16 bytes), walking the buffer from a per-wave start, and
+// waits for its loads every round.  One word of LDS per wave goes to out.
+constexpr int kDmaLoads = 8;
+constexpr int kDmaWaves = 8;
+
+__global__ __launch_bounds__(kDmaWaves * 64) void lds_dma_kernel(const char *__restrict__ buf,
+                                                                 int64_t chunks, int iters,
+                                                                 uint32_t *__restrict__ out)
+{
+    __shared__ __align__(16) char lds[kDmaWaves * kDmaLoads * 1024];
+    const int wave = (int)threadIdx.x >> 6, lane = (int)threadIdx.x & 63;
+    char *mine = lds + wave * kDmaLoads * 1024;
+    // chunk = one KiB of the buffer (chunks >= kDmaLoads); this wave starts
+    // at a chunk of its own
+    int64_t c = ((int64_t)blockIdx.x * kDmaWaves + wave) * kDmaLoads % chunks;
+    for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int l = 0; l < kDmaLoads; ++l) {
+            const int64_t cc = c + l < chunks ? c + l : c + l - chunks;
+            __builtin_amdgcn_global_load_lds((const void *)(buf + cc * 1024 + lane * 16),
+                                             (__attribute__((address_space(3))) void *)(mine + l * 1024),
+                                             16, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this round's loads are in LDS
+        c = c + kDmaLoads < chunks ? c + kDmaLoads : c + kDmaLoads - chunks;
+    }
+    __syncthreads();
+    if (lane == 0)
+        out[blockIdx.x * kDmaWaves + wave] = *(const uint32_t *)mine;
+}
+
+}  // namespace
+
+extern "C" {
+
+// n_vec 16-byte vectors, workgroups of `block` threads (64, 128 or 256);
+// sink must hold grid * block words (mode 1).
+int ceil_stream(const void *src, void *dst, int64_t n_vec, int mode, int grid, int block,
+                void *sink, void *stream)
+{
+    if (n_vec < 0 || grid <= 0 || mode < 0 || mode > 2 || (block != 64 && block != 128 && block != 256))
+        return -1;
+    hipLaunchKernelGGL(stream_kernel, dim3(grid), dim3(block), 0, (hipStream_t)stream,
+                       (const u32x4 *)src, (u32x4 *)dst, n_vec, mode, (uint32_t *)sink);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// out must hold grid * 256 floats.  Flops per launch: grid * 4 waves * iters
+// * kChains * 32768.
+int ceil_mfma(int grid, int iters, float *out, void *stream)
+{
+    if (grid <= 0 || iters <= 0)
+        return -1;
+    hipLaunchKernelGGL(mfma_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+int ceil_mfma_chains(void) { return kChains; }
+
+// buf holds chunks KiB (chunks >= kDmaLoads); out must hold grid * 8 words.  Bytes
+// per launch: grid * 8 waves * iters * kDmaLoads KiB.
+int ceil_lds_dma(const void *buf, int64_t chunks, int grid, int iters, uint32_t *out, void *stream)
+{
+    if (chunks < kDmaLoads || grid <= 0 || iters <= 0)
+        return -1;
+    hipLaunchKernelGGL(lds_dma_kernel, dim3(grid), dim3(kDmaWaves * 64), 0, (hipStream_t)stream,
+                       (const char *)buf, chunks, iters, out);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+int ceil_lds_dma_loads(void) { return kDmaLoads; }
+int ceil_lds_dma_waves(void) { return kDmaWaves; }
+
+}  // extern "C"

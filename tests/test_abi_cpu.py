@@ -149,3 +149,17 @@ def test_binding_raises_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(mx, "_lib", None)
     with pytest.raises(RuntimeError, match="no fallback"):
         mx.moonep_check_shape(mx.Shape(4, 16, 128, 2, 64))
+
+
+def test_ceilings_library_loads_outside_the_c_abi():
+    """bench.py --ceilings loads its own library; none of its symbols is part
+    of libmoonep's C-ABI (CPU only: nothing is launched)."""
+    from load_balancing_amd import build
+    if not os.path.exists(build.CEIL_LIB):
+        build.build()
+    C = ctypes.CDLL(build.CEIL_LIB)
+    for n in ("ceil_stream", "ceil_mfma", "ceil_mfma_chains", "ceil_lds_dma", "ceil_lds_dma_loads",
+              "ceil_lds_dma_waves"):
+        assert hasattr(C, n), n
+    assert C.ceil_mfma_chains() > 0 and C.ceil_lds_dma_loads() > 0 and C.ceil_lds_dma_waves() > 0
+    assert not any(n.startswith("ceil_") for n in mx.EXPORTS)
