@@ -458,17 +458,25 @@ def map_study(reps=5, seed=0):
                       "cache": "untimed 512 MiB read before each call"}), flush=True)
 
 
-def ceilings(reps=9):
+def ceilings(reps=9, parts=("hbm", "mfma", "lds_dma", "dense_gemm")):
     """Machine ceilings on this GPU, from libmoonep_ceilings.so (kernels of
-    their own, outside libmoonep): 1 GiB non-temporal streams (copy, read-only,
-    write-only) from an evicted cache, the best of 64-, 128- and 256-thread
-    workgroups at 1-32 waves per CU;
-    the bf16 matrix pipe (32x32x16 MFMAs on
-    register operands, 8 independent accumulators per wave, no memory
-    traffic) at 1 and 4 waves per SIMD; and LDS-DMA (16-byte global_load_lds)
-    from a 2 MiB buffer that stays in the L2, 8 or 16 waves per CU, 8 KiB per
-    wave in flight.  Median of `reps` launches each, HIP events on the launching
-    stream.  Prints one JSON line."""
+    their own, outside libmoonep): 1 GiB streams (copy, read-only,
+    write-only) with non-temporal loads, the best of 4 or 8 16-byte vectors
+    per thread in flight, grid-stride or per-wave runs, 64- or 256-thread
+    workgroups at 1-32 waves per CU.  Each stream is timed two ways:
+    from an evicted cache (an untimed 512 MiB read before each launch) and
+    back to back (no eviction between launches, so each launch pays for the
+    dirty lines the previous one left in the L2 and the MALL).  Write-back
+    stores from an evicted cache leave their last dirty lines to the next
+    kernel (the eviction), so that figure is reported but is no ceiling.
+    Then the bf16 matrix pipe (32x32x16 MFMAs on register operands, 8
+    independent accumulators per wave, no memory traffic) at 1 and 4 waves
+    per SIMD; LDS-DMA (16-byte global_load_lds) from a 2 MiB buffer that
+    stays in the L2, 8 or 16 waves per CU, 8 KiB per wave in flight; and,
+    for reference, the vendor library's dense bf16 GEMM (torch.matmul, which
+    calls hipBLASLt) at the expert GEMM's total sizes.  Median of `reps`
+    launches each, HIP events on the launching stream.  `parts` picks which
+    of hbm, mfma, lds_dma and dense_gemm run.  Prints one JSON line."""
     import ctypes
 
     import torch
@@ -480,7 +488,7 @@ def ceilings(reps=9):
         raise RuntimeError(f"{path} is missing: run __graft_entry__.build() first")
     L = ctypes.CDLL(path)
     VP, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    L.ceil_stream.argtypes = [VP, VP, I64, I, I, I, VP, VP]
+    L.ceil_stream.argtypes = [VP, VP, I64, I, I, I, I, I, I, VP, VP]
     L.ceil_mfma.argtypes = [I, I, VP, VP]
     L.ceil_lds_dma.argtypes = [VP, I64, I, I, VP, VP]
     dev = torch.device("cuda:0")
@@ -489,7 +497,9 @@ def ceilings(reps=9):
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
     flush_buf = torch.ones(1 << 27, dtype=torch.float32, device=dev)
 
-    def timed(fn, flush):
+    def timed(fn, flush, warm=0):
+        for _ in range(warm):
+            assert fn() == 0
         ts = []
         for _ in range(reps):
             if flush:
@@ -504,25 +514,58 @@ def ceilings(reps=9):
         return sorted(ts)[reps // 2]
 
     out = {}
+    if "hbm" in parts:
+        ceil_hbm_streams(L, dev, sp, cus, timed, out)
+    if "mfma" in parts:
+        ceil_mfma_pipe(L, dev, sp, cus, timed, out)
+    if "lds_dma" in parts:
+        ceil_lds_dma(L, dev, sp, cus, timed, out)
+    if "dense_gemm" in parts:
+        ceil_dense_gemm(dev, timed, out)
+    out["peaks"] = {"hbm_GBps": 8000.0, "mfma_bf16_TFLOPs": 2500.0}
+    print(json.dumps({"ceilings": out, "reps": reps, "cus": cus}), flush=True)
+
+
+def ceil_hbm_streams(L, dev, sp, cus, timed, out):
+    """1 GiB copy, read-only and write-only streams (see ceilings)."""
+    import itertools
+
+    import torch
+
     nbytes = 1 << 30
     src = torch.ones(nbytes // 4, dtype=torch.int32, device=dev)
     dst = torch.empty_like(src)
     sink = torch.empty(cus * 32 * 64, dtype=torch.int32, device=dev)  # one word per thread
     nvec = nbytes // 16
     for mode, name, moved in ((0, "copy", 2 * nbytes), (1, "read", nbytes), (2, "write", nbytes)):
-        best = None
-        for block in (64, 128, 256):
-            for waves_per_cu in (1, 2, 4, 8, 16, 32):  # the best configuration is reported
+        policies = ((1, "nt", True), (1, "nt_back_to_back", False))
+        if mode != 1:  # stores: write-back as well
+            policies += ((0, "wb_back_to_back", False), (0, "wb_evicted_defers_writeback", True))
+        for nt_store, tag, flush in policies:
+            best = None
+            for unroll, chunks, block, waves_per_cu in itertools.product((4, 8), (0, 1), (64, 256),
+                                                                          (1, 2, 4, 8, 16, 32)):
                 g = cus * waves_per_cu * 64 // block
                 if g < cus:
                     continue
-                t = timed(lambda: L.ceil_stream(src.data_ptr(), dst.data_ptr(), nvec, mode, g, block,
-                                                sink.data_ptr(), sp), True)
+                t = timed(lambda: L.ceil_stream(src.data_ptr(), dst.data_ptr(), nvec, mode, unroll, nt_store,
+                                                chunks, g, block, sink.data_ptr(), sp), flush,
+                          warm=0 if flush else 2)
                 if best is None or t < best[0]:
-                    best = (t, block, waves_per_cu)
-        out[f"hbm_{name}_GBps"] = round(moved / best[0] / 1e9, 1)
-        out[f"hbm_{name}_config"] = f"{best[1]}-thread workgroups, {best[2]} waves per CU"
+                    best = (t, unroll, chunks, block, waves_per_cu)
+            out[f"hbm_{name}_{tag}_GBps"] = round(moved / best[0] / 1e9, 1)
+            out[f"hbm_{name}_{tag}_config"] = (
+                f"{best[1]} vectors per thread, {'per-wave runs' if best[2] else 'grid-stride'}, "
+                f"{best[3]}-thread workgroups, {best[4]} waves per CU")
+        out[f"hbm_{name}_GBps"] = max(out[f"hbm_{name}_{t}_GBps"] for t in
+                                      ("nt", "nt_back_to_back", "wb_back_to_back") if f"hbm_{name}_{t}_GBps" in out)
     del src, dst
+
+
+def ceil_mfma_pipe(L, dev, sp, cus, timed, out):
+    """Independent bf16 MFMAs on register operands, 1 and 4 waves per SIMD."""
+    import torch
+
     chains = L.ceil_mfma_chains()
     iters = 4096
     for waves_per_simd in (1, 4):
@@ -531,6 +574,12 @@ def ceilings(reps=9):
         t = timed(lambda: L.ceil_mfma(g, iters, res.data_ptr(), sp), False)
         flops = g * 4 * iters * chains * 32 * 32 * 16 * 2
         out[f"mfma_bf16_TFLOPs_{waves_per_simd}_wave_per_simd"] = round(flops / t / 1e12, 1)
+
+
+def ceil_lds_dma(L, dev, sp, cus, timed, out):
+    """LDS-DMA from a 2 MiB buffer held in the L2, 1 and 2 workgroups per CU."""
+    import torch
+
     chunks = 2048  # 2 MiB
     buf = torch.ones(chunks * 256, dtype=torch.int32, device=dev)
     loads, waves = L.ceil_lds_dma_loads(), L.ceil_lds_dma_waves()
@@ -542,8 +591,29 @@ def ceilings(reps=9):
         t = timed(lambda: L.ceil_lds_dma(buf.data_ptr(), chunks, g, dma_iters, res.data_ptr(), sp), False)
         out[f"lds_dma_from_l2_GBps_{per_cu}_workgroup_per_cu"] = round(
             g * waves * dma_iters * loads * 1024 / t / 1e9, 1)
-    out["peaks"] = {"hbm_GBps": 8000.0, "mfma_bf16_TFLOPs": 2500.0}
-    print(json.dumps({"ceilings": out, "reps": reps, "cus": cus}), flush=True)
+
+
+def ceil_dense_gemm(dev, timed, out):
+    """The vendor library's dense bf16 GEMM (torch.matmul -> hipBLASLt) at the
+    expert GEMM's total sizes: rows x in -> out with one weight matrix for
+    all rows (the grouped GEMM has one per expert), the weight stored
+    [out, in] as the expert weights are."""
+    import torch
+
+    for tag, (m, k, n) in (("sweep_gate", (262144, 2048, 1408)), ("sweep_down", (262144, 1408, 2048)),
+                           ("dsv3_gate", (1048576, 7168, 2048)), ("dsv3_down", (1048576, 2048, 7168))):
+        a = torch.randn(m, k, device=dev, dtype=torch.bfloat16)
+        w = torch.randn(n, k, device=dev, dtype=torch.bfloat16)
+        wt = w.t()
+        c = torch.empty(m, n, device=dev, dtype=torch.bfloat16)
+
+        def dense():
+            torch.matmul(a, wt, out=c)
+            return 0
+
+        t = timed(dense, False, warm=2)
+        out[f"dense_gemm_hipblaslt_{tag}_TFLOPs"] = round(2 * m * k * n / t / 1e12, 1)
+        del a, w, wt, c
 
 
 def main():
@@ -569,15 +639,20 @@ def main():
     ap.add_argument("--map-study", action="store_true",
                     help="diagnostic: time the movers over non-plan destination maps (identity, "
                          "uniform expert, random permutation) beside two plans, then exit")
-    ap.add_argument("--ceilings", action="store_true",
+    ap.add_argument("--ceilings", nargs="?", const="hbm,mfma,lds_dma,dense_gemm", default=None,
                     help="diagnostic: measure the machine ceilings (HBM streams, the bf16 matrix "
-                         "pipe, LDS-DMA from the L2) with libmoonep_ceilings.so, then exit")
+                         "pipe, LDS-DMA from the L2) with libmoonep_ceilings.so and the vendor "
+                         "library's dense GEMM, then exit; optionally a comma list of those parts")
     args = ap.parse_args()
     if args.map_study:
         map_study()
         return
-    if args.ceilings:
-        ceilings()
+    if args.ceilings is not None:
+        parts = set(args.ceilings.split(","))
+        unknown = parts - {"hbm", "mfma", "lds_dma", "dense_gemm"}
+        if unknown:
+            raise SystemExit(f"--ceilings: unknown part(s) {sorted(unknown)}")
+        ceilings(parts=parts)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark measures one GPU: R logical ranks are slices of one "

@@ -16,45 +16,66 @@ __device__ __forceinline__ u32x4 load_nt(const u32x4 *p) { return __builtin_nont
 __device__ __forceinline__ void store_nt(u32x4 *p, u32x4 v) { __builtin_nontemporal_store(v, p); }
 
 // mode 0: dst = src; mode 1: read src, one word per thread to sink; mode 2:
-// write dst.  16-byte non-temporal vectors, grid-stride, kUnroll vectors per
-// thread in flight (all loads of a round issued before its stores).
-constexpr int kUnroll = 4;
-
+// write dst.  16-byte vectors, U vectors per thread in flight (all loads of a
+// round issued before its stores), non-temporal loads.  NT_STORE picks
+// non-temporal or write-back stores.  WAVE_CHUNKS = false: grid-stride per
+// thread (a wave's U vectors are a grid stride apart); true: each wave owns
+// runs of U contiguous KiB, the runs a grid of waves apart.
+template <int U, bool NT_STORE, bool WAVE_CHUNKS>
 __global__ __launch_bounds__(256) void stream_kernel(const u32x4 *__restrict__ src,
                                                      u32x4 *__restrict__ dst, int64_t n,
                                                      int mode, uint32_t *__restrict__ sink)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    const int64_t i0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t tid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t threads = (int64_t)gridDim.x * blockDim.x;
+    // first vector of this thread, distance between its U vectors, and
+    // distance between its rounds
+    const int64_t i0 = WAVE_CHUNKS ? (tid >> 6) * U * 64 + (tid & 63) : tid;
+    const int64_t ustride = WAVE_CHUNKS ? 64 : threads;
+    const int64_t step = WAVE_CHUNKS ? (threads >> 6) * U * 64 : U * threads;
     uint32_t acc = 0;
-    for (int64_t i = i0; i < n; i += kUnroll * stride) {
-        u32x4 v[kUnroll];
+    for (int64_t i = i0; i < n; i += step) {
+        u32x4 v[U];
         if (mode != 2) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t j = i + u * stride;
+            for (int u = 0; u < U; ++u) {
+                const int64_t j = i + u * ustride;
                 v[u] = j < n ? load_nt(src + j) : u32x4{0u, 0u, 0u, 0u};
             }
         } else {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+            for (int u = 0; u < U; ++u)
                 v[u] = u32x4{(uint32_t)i, (uint32_t)u, 2u, 3u};
         }
         if (mode == 1) {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u)
+            for (int u = 0; u < U; ++u)
                 acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
         } else {
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int64_t j = i + u * stride;
-                if (j < n)
-                    store_nt(dst + j, v[u]);
+            for (int u = 0; u < U; ++u) {
+                const int64_t j = i + u * ustride;
+                if (j < n) {
+                    if (NT_STORE)
+                        store_nt(dst + j, v[u]);
+                    else
+                        dst[j] = v[u];
+                }
             }
         }
     }
     if (mode == 1)
-        sink[i0] = acc;  // sink holds one word per launched thread
+        sink[tid] = acc;  // sink holds one word per launched thread
+}
+
+typedef void (*stream_fn)(const u32x4 *, u32x4 *, int64_t, int, uint32_t *);
+
+template <int U>
+stream_fn pick_stream(int nt_store, int wave_chunks)
+{
+    if (nt_store)
+        return wave_chunks ? stream_kernel<U, true, true> : stream_kernel<U, true, false>;
+    return wave_chunks ? stream_kernel<U, false, true> : stream_kernel<U, false, false>;
 }
 
 // kChains independent 32x32x16 bf16 MFMA accumulators per wave, `iters`
@@ -126,15 +147,19 @@ __global__ __launch_bounds__(kDmaWaves * 64) void lds_dma_kernel(const char *__r
 
 extern "C" {
 
-// n_vec 16-byte vectors, workgroups of `block` threads (64, 128 or 256);
-// sink must hold grid * block words (mode 1).
-int ceil_stream(const void *src, void *dst, int64_t n_vec, int mode, int grid, int block,
-                void *sink, void *stream)
+// n_vec 16-byte vectors, workgroups of `block` threads (64, 128 or 256),
+// `unroll` vectors per thread in flight (4 or 8), non-temporal or write-back
+// stores, grid-stride or per-wave runs (see stream_kernel); sink must hold
+// grid * block words (mode 1).
+int ceil_stream(const void *src, void *dst, int64_t n_vec, int mode, int unroll, int nt_store,
+                int wave_chunks, int grid, int block, void *sink, void *stream)
 {
-    if (n_vec < 0 || grid <= 0 || mode < 0 || mode > 2 || (block != 64 && block != 128 && block != 256))
+    if (n_vec < 0 || grid <= 0 || mode < 0 || mode > 2 || (block != 64 && block != 128 && block != 256) ||
+        (unroll != 4 && unroll != 8))
         return -1;
-    hipLaunchKernelGGL(stream_kernel, dim3(grid), dim3(block), 0, (hipStream_t)stream,
-                       (const u32x4 *)src, (u32x4 *)dst, n_vec, mode, (uint32_t *)sink);
+    const stream_fn f = unroll == 4 ? pick_stream<4>(nt_store, wave_chunks) : pick_stream<8>(nt_store, wave_chunks);
+    hipLaunchKernelGGL(f, dim3(grid), dim3(block), 0, (hipStream_t)stream, (const u32x4 *)src, (u32x4 *)dst,
+                       n_vec, mode, (uint32_t *)sink);
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

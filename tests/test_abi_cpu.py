@@ -163,3 +163,8 @@ def test_ceilings_library_loads_outside_the_c_abi():
         assert hasattr(C, n), n
     assert C.ceil_mfma_chains() > 0 and C.ceil_lds_dma_loads() > 0 and C.ceil_lds_dma_waves() > 0
     assert not any(n.startswith("ceil_") for n in mx.EXPORTS)
+    # the stream entry checks its arguments before any launch
+    VP, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    C.ceil_stream.argtypes = [VP, VP, I64, I, I, I, I, I, I, VP, VP]
+    for mode, unroll, grid, block in ((3, 4, 1, 64), (0, 3, 1, 64), (0, 4, 0, 64), (0, 8, 1, 96)):
+        assert C.ceil_stream(None, None, 16, mode, unroll, 1, 0, grid, block, None, None) == -1
