@@ -43,6 +43,12 @@ granularity, so it has no GEMM leg.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload sweep|dsv3|adversarial|tiny]
                     [--no-cpu-baseline]
+
+Diagnostics (each prints one JSON line and exits): --ceilings [hbm,mfma,lds_dma,dense_gemm]
+measures the machine ceilings the kernels are judged against (HBM streams, the
+bf16 matrix pipe, LDS-DMA from the L2, the vendor dense GEMM at the expert
+GEMM's sizes); --map-study times the four movers over planned and synthetic
+destination maps.
 """
 import argparse
 import hashlib
