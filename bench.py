@@ -44,9 +44,9 @@ granularity, so it has no GEMM leg.
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload sweep|dsv3|adversarial|tiny]
                     [--no-cpu-baseline]
 
-Diagnostics (each prints one JSON line and exits): --ceilings [hbm,mfma,lds_dma,dense_gemm]
-measures the machine ceilings the kernels are judged against (HBM streams, the
-bf16 matrix pipe, LDS-DMA from the L2, the vendor dense GEMM at the expert
+Diagnostics (each prints one JSON line and exits): --ceilings [hbm,rows,mfma,lds_dma,dense_gemm]
+measures the machine ceilings the kernels are judged against (HBM streams,
+copies of 4 KiB rows at random positions, the bf16 matrix pipe, LDS-DMA from the L2, the vendor dense GEMM at the expert
 GEMM's sizes); --map-study times the four movers over planned and synthetic
 destination maps.
 """
@@ -464,7 +464,7 @@ def map_study(reps=5, seed=0):
                       "cache": "untimed 512 MiB read before each call"}), flush=True)
 
 
-def ceilings(reps=9, parts=("hbm", "mfma", "lds_dma", "dense_gemm")):
+def ceilings(reps=9, parts=("hbm", "rows", "mfma", "lds_dma", "dense_gemm")):
     """Machine ceilings on this GPU, from libmoonep_ceilings.so (kernels of
     their own, outside libmoonep): 1 GiB streams (copy, read-only,
     write-only) with non-temporal loads, the best of 4 or 8 16-byte vectors
@@ -482,7 +482,8 @@ def ceilings(reps=9, parts=("hbm", "mfma", "lds_dma", "dense_gemm")):
     for reference, the vendor library's dense bf16 GEMM (torch.matmul, which
     calls hipBLASLt) at the expert GEMM's total sizes.  Median of `reps`
     launches each, HIP events on the launching stream.  `parts` picks which
-    of hbm, mfma, lds_dma and dense_gemm run.  Prints one JSON line."""
+    of hbm, rows (4 KiB rows at random positions, see ceil_rows), mfma,
+    lds_dma and dense_gemm run.  Prints one JSON line."""
     import ctypes
 
     import torch
@@ -495,6 +496,7 @@ def ceilings(reps=9, parts=("hbm", "mfma", "lds_dma", "dense_gemm")):
     L = ctypes.CDLL(path)
     VP, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     L.ceil_stream.argtypes = [VP, VP, I64, I, I, I, I, I, I, VP, VP]
+    L.ceil_rows.argtypes = [VP, VP, VP, VP, I64, I, I, I, VP, VP]
     L.ceil_mfma.argtypes = [I, I, VP, VP]
     L.ceil_lds_dma.argtypes = [VP, I64, I, I, VP, VP]
     dev = torch.device("cuda:0")
@@ -522,6 +524,8 @@ def ceilings(reps=9, parts=("hbm", "mfma", "lds_dma", "dense_gemm")):
     out = {}
     if "hbm" in parts:
         ceil_hbm_streams(L, dev, sp, cus, timed, out)
+    if "rows" in parts:
+        ceil_rows(L, dev, sp, cus, timed, out)
     if "mfma" in parts:
         ceil_mfma_pipe(L, dev, sp, cus, timed, out)
     if "lds_dma" in parts:
@@ -565,6 +569,46 @@ def ceil_hbm_streams(L, dev, sp, cus, timed, out):
                 f"{best[3]}-thread workgroups, {best[4]} waves per CU")
         out[f"hbm_{name}_GBps"] = max(out[f"hbm_{name}_{t}_GBps"] for t in
                                       ("nt", "nt_back_to_back", "wb_back_to_back") if f"hbm_{name}_{t}_GBps" in out)
+    del src, dst
+
+
+def ceil_rows(L, dev, sp, cus, timed, out):
+    """Rows of 4 KiB (2048 bf16) at the sweep's dispatch-buffer size (262,144
+    rows, 1 GiB): copies sequential to sequential, random source rows to
+    sequential ones (a gather), sequential to random (a scatter) and random to
+    random (two independent permutations), and random rows written only or
+    read only; non-temporal, each from an evicted cache, the best of 64-thread
+    workgroups (4 vectors per thread) and 256-thread workgroups (1 vector per
+    thread) at 4-32 waves per CU.  These are the access patterns of the
+    scattered movers without their arithmetic."""
+    import itertools
+
+    import torch
+
+    nrows, row_vecs = 262144, 256
+    src = torch.ones(nrows * row_vecs * 4, dtype=torch.int32, device=dev)
+    dst = torch.empty_like(src)
+    sink = torch.empty(cus * 32 * 64, dtype=torch.int32, device=dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    p1 = torch.randperm(nrows, generator=gen, device=dev).to(torch.int32)
+    p2 = torch.randperm(nrows, generator=gen, device=dev).to(torch.int32)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    row_bytes = row_vecs * 16
+    patterns = (("copy_sequential", src, None, dst, None), ("gather", src, p1, dst, None),
+                ("scatter", src, None, dst, p1), ("copy_random", src, p1, dst, p2),
+                ("write_random", None, None, dst, p1), ("read_random", src, p1, None, None))
+    for name, s_, si, d_, di in patterns:
+        moved = nrows * row_bytes * ((s_ is not None) + (d_ is not None))
+        best = None
+        for block, waves_per_cu in itertools.product((64, 256), (4, 8, 12, 16, 24, 32)):
+            g = cus * waves_per_cu * 64 // block
+            t = timed(lambda: L.ceil_rows(ptr(s_), ptr(d_), ptr(si), ptr(di), nrows, row_vecs, g, block,
+                                          sink.data_ptr(), sp), True)
+            if best is None or t < best[0]:
+                best = (t, block, waves_per_cu)
+        out[f"hbm_rows_{name}_GBps"] = round(moved / best[0] / 1e9, 1)
+        out[f"hbm_rows_{name}_config"] = f"{best[1]}-thread workgroups, {best[2]} waves per CU"
     del src, dst
 
 
@@ -645,7 +689,7 @@ def main():
     ap.add_argument("--map-study", action="store_true",
                     help="diagnostic: time the movers over non-plan destination maps (identity, "
                          "uniform expert, random permutation) beside two plans, then exit")
-    ap.add_argument("--ceilings", nargs="?", const="hbm,mfma,lds_dma,dense_gemm", default=None,
+    ap.add_argument("--ceilings", nargs="?", const="hbm,rows,mfma,lds_dma,dense_gemm", default=None,
                     help="diagnostic: measure the machine ceilings (HBM streams, the bf16 matrix "
                          "pipe, LDS-DMA from the L2) with libmoonep_ceilings.so and the vendor "
                          "library's dense GEMM, then exit; optionally a comma list of those parts")
@@ -655,7 +699,7 @@ def main():
         return
     if args.ceilings is not None:
         parts = set(args.ceilings.split(","))
-        unknown = parts - {"hbm", "mfma", "lds_dma", "dense_gemm"}
+        unknown = parts - {"hbm", "rows", "mfma", "lds_dma", "dense_gemm"}
         if unknown:
             raise SystemExit(f"--ceilings: unknown part(s) {sorted(unknown)}")
         ceilings(parts=parts)

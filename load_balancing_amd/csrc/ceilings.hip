@@ -1,6 +1,7 @@
 // ceilings.hip -- microbenchmarks of the machine ceilings the kernels are
-// judged against: HBM streams (copy, read-only, write-only), the matrix
-// pipe's bf16 rate, and LDS-DMA from data that sits in the L2.  Built as its
+// judged against: HBM streams (copy, read-only, write-only), copies of 4 KiB
+// rows at random positions, the matrix pipe's bf16 rate, and LDS-DMA from
+// data that sits in the L2.  Built as its
 // own library (libmoonep_ceilings.so), outside the C-ABI of libmoonep.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
@@ -76,6 +77,49 @@ stream_fn pick_stream(int nt_store, int wave_chunks)
     if (nt_store)
         return wave_chunks ? stream_kernel<U, true, true> : stream_kernel<U, true, false>;
     return wave_chunks ? stream_kernel<U, false, true> : stream_kernel<U, false, false>;
+}
+
+// Rows of `row_vecs` 16-byte vectors: row i of dst (row dst_idx[i], or i when
+// dst_idx is null) = row src_idx[i] of src (or i when src_idx is null).  A
+// null src writes a constant (write-only); a null dst reads only, one word per
+// thread to sink.  One workgroup per row per round, a grid-stride loop over
+// rows; each thread moves row_vecs / blockDim.x vectors, all loads issued
+// before the stores.  With random indices this is the access pattern of the
+// scattered movers (4 KiB rows at random positions) without their arithmetic.
+template <int U>
+__global__ __launch_bounds__(256) void rows_kernel(const u32x4 *__restrict__ src, u32x4 *__restrict__ dst,
+                                                   const int32_t *__restrict__ src_idx,
+                                                   const int32_t *__restrict__ dst_idx, int64_t nrows,
+                                                   int32_t row_vecs, uint32_t *__restrict__ sink)
+{
+    uint32_t acc = 0;
+    for (int64_t r = blockIdx.x; r < nrows; r += gridDim.x) {
+        u32x4 v[U];
+        if (src) {
+            const int64_t rs = src_idx ? src_idx[r] : r;
+            const u32x4 *sp = src + rs * row_vecs;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = load_nt(sp + u * (int)blockDim.x + (int)threadIdx.x);
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = u32x4{(uint32_t)r, (uint32_t)u, 2u, 3u};
+        }
+        if (dst) {
+            const int64_t rd = dst_idx ? dst_idx[r] : r;
+            u32x4 *dp = dst + rd * row_vecs;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                store_nt(dp + u * (int)blockDim.x + (int)threadIdx.x, v[u]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+        }
+    }
+    if (!dst)
+        sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = acc;  // one word per launched thread
 }
 
 // kChains independent 32x32x16 bf16 MFMA accumulators per wave, `iters`
@@ -160,6 +204,29 @@ int ceil_stream(const void *src, void *dst, int64_t n_vec, int mode, int unroll,
     const stream_fn f = unroll == 4 ? pick_stream<4>(nt_store, wave_chunks) : pick_stream<8>(nt_store, wave_chunks);
     hipLaunchKernelGGL(f, dim3(grid), dim3(block), 0, (hipStream_t)stream, (const u32x4 *)src, (u32x4 *)dst,
                        n_vec, mode, (uint32_t *)sink);
+    return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// nrows rows of row_vecs 16-byte vectors; src_idx / dst_idx (device, nrows
+// entries each, values in [0, nrows)) or null for the identity; src null:
+// write-only, dst null: read-only with sink holding grid * block words (one
+// of src and dst must be set); block threads per row (64 or 256) with
+// row_vecs == U * block for U in {1, 4}.
+int ceil_rows(const void *src, void *dst, const int32_t *src_idx, const int32_t *dst_idx, int64_t nrows,
+              int row_vecs, int grid, int block, void *sink, void *stream)
+{
+    if (nrows < 0 || grid <= 0 || (block != 64 && block != 256) || row_vecs <= 0 || row_vecs % block != 0 ||
+        (!src && !dst) || (!dst && !sink))
+        return -1;
+    const int u = row_vecs / block;
+    if (u == 1)
+        hipLaunchKernelGGL(rows_kernel<1>, dim3(grid), dim3(block), 0, (hipStream_t)stream, (const u32x4 *)src,
+                           (u32x4 *)dst, src_idx, dst_idx, nrows, row_vecs, (uint32_t *)sink);
+    else if (u == 4)
+        hipLaunchKernelGGL(rows_kernel<4>, dim3(grid), dim3(block), 0, (hipStream_t)stream, (const u32x4 *)src,
+                           (u32x4 *)dst, src_idx, dst_idx, nrows, row_vecs, (uint32_t *)sink);
+    else
+        return -1;
     return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

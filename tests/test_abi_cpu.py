@@ -158,7 +158,7 @@ def test_ceilings_library_loads_outside_the_c_abi():
     if not os.path.exists(build.CEIL_LIB):
         build.build()
     C = ctypes.CDLL(build.CEIL_LIB)
-    for n in ("ceil_stream", "ceil_mfma", "ceil_mfma_chains", "ceil_lds_dma", "ceil_lds_dma_loads",
+    for n in ("ceil_stream", "ceil_rows", "ceil_mfma", "ceil_mfma_chains", "ceil_lds_dma", "ceil_lds_dma_loads",
               "ceil_lds_dma_waves"):
         assert hasattr(C, n), n
     assert C.ceil_mfma_chains() > 0 and C.ceil_lds_dma_loads() > 0 and C.ceil_lds_dma_waves() > 0
@@ -168,3 +168,9 @@ def test_ceilings_library_loads_outside_the_c_abi():
     C.ceil_stream.argtypes = [VP, VP, I64, I, I, I, I, I, I, VP, VP]
     for mode, unroll, grid, block in ((3, 4, 1, 64), (0, 3, 1, 64), (0, 4, 0, 64), (0, 8, 1, 96)):
         assert C.ceil_stream(None, None, 16, mode, unroll, 1, 0, grid, block, None, None) == -1
+    C.ceil_rows.argtypes = [VP, VP, VP, VP, I64, I, I, I, VP, VP]
+    fake = ctypes.c_void_p(16)  # never dereferenced: every call below is refused first
+    for s_, d_, row_vecs, block, sink in ((None, None, 256, 256, None), (fake, None, 256, 256, None),
+                                          (fake, fake, 256, 128, None), (fake, fake, 192, 64, None),
+                                          (fake, fake, 512, 256, None)):
+        assert C.ceil_rows(s_, d_, None, None, 8, row_vecs, 1, block, sink, None) == -1
